@@ -1,0 +1,271 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+* hand-worked example of the pages' bias broadcast / ReLU / mask / DRELU_BGRAD
+  definitions (tests/golden/worked_example.json);
+* brute force on tiny inputs: math.fsum exact sums and Fraction rounding
+  (tests/brute.py) for every epilogue, both dtypes, both B layouts, both bias
+  orientations, ragged sizes;
+* exact integer arithmetic at large K;
+* GELU against standard-normal-table values (tests/golden/normal_cdf.json) and
+  its symmetry gelu(z) - gelu(-z) = z;
+* rounding against hand-derived bit patterns (tests/golden/rounding_cases.json)
+  and against numpy's own double->half conversion;
+* invariants that relate the epilogues to each other.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import brute
+import workloads as wl
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _f16(vals):
+    return np.asarray(vals, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+# ---------------------------------------------------------------- worked example
+def test_worked_example_all_epilogues():
+    g = _golden("worked_example.json")
+    W = _f16(g["W"]); X = _f16(g["X"])
+    bcol = _f16(g["bias_col"]); brow = _f16(g["bias_row"])
+    ex = g["expected"]
+    M, K, N = 2, 3, 2
+
+    def run(epi, bias=None, per_col=False, aux=None):
+        return O.gemm_epilogue(W, X, bias, aux, M, N, K, "f16", epi, False, per_col)
+
+    def vals(r):
+        return O.decode_f16(r.out).tolist()
+
+    assert vals(run("DEFAULT")) == ex["DEFAULT"]
+    assert vals(run("BIAS", bcol)) == ex["BIAS"]
+    assert vals(run("RELU_BIAS", bcol)) == ex["RELU_BIAS"]
+    r = run("RELU_AUX_BIAS", bcol)
+    assert vals(r) == ex["RELU_BIAS"]
+    assert r.mask[:, 0].tolist() == ex["RELU_AUX_BIAS_mask_words"]
+    assert np.all(r.mask[:, 1:] == 0)
+    assert vals(run("BIAS", brow, per_col=True)) == ex["BIAS_PER_COL"]
+    aux = np.zeros((M, O.aux_ld_words(N)), dtype=np.uint32)
+    aux[:, 0] = ex["DRELU_BGRAD_mask_words"]
+    r = run("DRELU_BGRAD", aux=aux)
+    assert vals(r) == ex["DRELU_BGRAD_dZ"]
+    assert r.bgrad.tolist() == ex["DRELU_BGRAD_bgrad"]
+
+
+# ---------------------------------------------------------------- brute force
+BRUTE_SHAPES = [(1, 1, 1), (3, 5, 8), (7, 6, 5), (8, 8, 8), (5, 33, 4), (2, 65, 3)]
+
+
+@pytest.mark.parametrize("epi", O.EPILOGUES)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_brute_force_tiny(epi, dtype):
+    for si, (M, N, K) in enumerate(BRUTE_SHAPES):
+        for b_trans in (False, True):
+            for per_col in (False, True):
+                seed = 77 + 13 * si + 2 * b_trans + per_col
+                c = wl.random_case(M, N, K, dtype, epi, b_trans, per_col, seed)
+                r = O.gemm_epilogue(c.A, c.B, c.bias, c.aux, M, N, K, dtype, epi,
+                                    b_trans, per_col)
+                mask_in = c.aux.tolist() if c.aux is not None else None
+                bout, bmask, bbgrad = brute.fused(
+                    c.A.ravel().tolist(), c.B.ravel().tolist(),
+                    None if c.bias is None else c.bias.tolist(), mask_in,
+                    M, N, K, dtype, epi, b_trans, per_col)
+                assert r.out.tolist() == bout, (M, N, K, b_trans, per_col)
+                if epi == "RELU_AUX_BIAS":
+                    assert np.array_equal(O.unpack_mask(r.mask, N), np.array(bmask, bool))
+                if epi == "DRELU_BGRAD":
+                    assert r.bgrad.tolist() == bbgrad
+
+
+def test_brute_force_row_subset():
+    M, N, K = 9, 7, 6
+    c = wl.random_case(M, N, K, "f16", "RELU_AUX_BIAS", False, False, 5)
+    full = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, "f16", "RELU_AUX_BIAS", False, False)
+    rows = np.array([0, 4, 8])
+    sub = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, "f16", "RELU_AUX_BIAS", False,
+                          False, rows=rows)
+    assert np.array_equal(sub.out, full.out[rows])
+    assert np.array_equal(sub.mask, full.mask[rows])
+    c = wl.random_case(M, N, K, "f16", "DRELU_BGRAD", False, False, 6)
+    full = O.gemm_epilogue(c.A, c.B, None, c.aux, M, N, K, "f16", "DRELU_BGRAD", False, False)
+    sub = O.gemm_epilogue(c.A, c.B, None, c.aux, M, N, K, "f16", "DRELU_BGRAD", False, False,
+                          rows=rows)
+    assert np.array_equal(sub.out, full.out[rows])
+    assert np.array_equal(sub.bgrad, full.bgrad)
+
+
+# ---------------------------------------------------------------- exact integers
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_integer_exact_large_k(dtype):
+    """A, B in {-3..3}: the exact result is an integer computed in Python ints."""
+    M, N, K = 4, 40, 4096
+    c = wl.random_case(M, N, K, dtype, "BIAS", False, True, 11, kind="int")
+    Ai = np.rint(O.decode(c.A, dtype)).astype(np.int64)
+    Bi = np.rint(O.decode(c.B, dtype)).astype(np.int64)
+    bi = np.rint(O.decode(c.bias, dtype)).astype(np.int64)
+    exact = [[sum(int(Ai[i, k]) * int(Bi[k, j]) for k in range(K)) + int(bi[j])
+              for j in range(N)] for i in range(M)]
+    r = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, dtype, "BIAS", False, True)
+    got = O.decode(r.out, dtype)
+    # the exact integers are within +-K*9+3, so they are exactly representable
+    # in fp16 only below 2048; compare against the exactly rounded integer
+    for i in range(M):
+        for j in range(N):
+            want = brute.f16_value(brute.f16_bits(float(exact[i][j]))) if dtype == "f16" \
+                else brute.bf16_value(brute.bf16_bits(float(exact[i][j])))
+            assert got[i, j] == want
+
+
+# ---------------------------------------------------------------- GELU
+def test_gelu_against_normal_table():
+    g = _golden("normal_cdf.json")
+    for z, phi in g["phi"]:
+        for zz, pp in ((z, phi), (-z, 1.0 - phi)):
+            want = zz * pp
+            got = float(O.gelu(np.array([zz]))[0])
+            assert abs(got - want) <= 1e-15 * max(1.0, abs(want)), (zz, got, want)
+
+
+def test_gelu_identities():
+    z = np.linspace(-12, 12, 2001)
+    g = O.gelu(z)
+    # gelu(z) - gelu(-z) = z * (Phi(z) + Phi(-z)) = z
+    assert np.max(np.abs(g - O.gelu(-z) - z)) < 1e-13
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    # large |z|: gelu -> z, gelu -> 0 from below
+    assert abs(O.gelu(np.array([12.0]))[0] - 12.0) < 1e-15
+    assert -1e-30 < O.gelu(np.array([-12.0]))[0] <= 0.0
+    # strictly below the identity and above the ReLU-minus-bound
+    assert np.all(g <= np.maximum(z, 0) + 1e-15)
+
+
+# ---------------------------------------------------------------- rounding
+def test_rounding_golden_cases():
+    g = _golden("rounding_cases.json")
+    for label, s, hexbits in g["f16"]:
+        x = float(s)
+        assert int(O.encode_f16(np.array([x]))[0]) == int(hexbits, 16), label
+        assert brute.f16_bits(x) == int(hexbits, 16), label
+    for label, s, hexbits in g["bf16"]:
+        x = float(s)
+        assert int(O.encode_bf16(np.array([x]))[0]) == int(hexbits, 16), label
+        assert brute.bf16_bits(x) == int(hexbits, 16), label
+
+
+def test_round_to_format_matches_numpy_half():
+    """The generic rounding used for bf16, instantiated for fp16, agrees with
+    numpy's independent double->half conversion on many values, including
+    subnormals, ties and overflow."""
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.standard_normal(200000) * np.exp2(rng.integers(-30, 17, 200000)),
+        (np.arange(-5000, 5000) + 0.5) * 2.0 ** -24,          # subnormal ties
+        1.0 + (np.arange(0, 4096) + 0.5) * 2.0 ** -10,         # normal ties
+        np.array([65504.0, 65519.99, 65520.0, 70000.0, -65520.0]),
+    ])
+    mine = O.round_to_format(x, 11, -14, 15)
+    ref = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(mine, ref, equal_nan=True)
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+def test_bf16_decode_encode_roundtrip():
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    v = O.decode_bf16(bits)
+    fin = np.isfinite(v)
+    back = O.encode_bf16(v[fin])
+    # -0 and +0 both decode to a zero; compare values for zeros
+    assert np.array_equal(O.decode_bf16(back), v[fin])
+
+
+# ---------------------------------------------------------------- invariants
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_invariants(dtype):
+    M, N, K = 37, 70, 48
+    c = wl.random_case(M, N, K, dtype, "BIAS", False, False, 21)
+    zero = np.zeros_like(c.bias)
+    d = O.gemm_epilogue(c.A, c.B, None, None, M, N, K, dtype, "DEFAULT", False, False)
+    b0 = O.gemm_epilogue(c.A, c.B, zero, None, M, N, K, dtype, "BIAS", False, False)
+    assert np.array_equal(d.out, b0.out)                      # zero bias == DEFAULT
+    b = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, dtype, "BIAS", False, False)
+    r = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, dtype, "RELU_AUX_BIAS", False, False)
+    rv = O.decode(r.out, dtype)
+    bv = O.decode(b.out, dtype)
+    assert np.all(rv >= 0)                                    # ReLU output >= 0
+    assert np.array_equal(rv, np.maximum(bv, 0))              # relu == max(bias_out, 0)
+    m = O.unpack_mask(r.mask, N)
+    assert np.array_equal(rv, np.where(m, bv, 0.0))           # relu == mask * z
+    assert np.array_equal(m, r.z > 0)
+    # B_TRANS with the transposed storage gives the same result
+    Bt = np.ascontiguousarray(c.B.reshape(K, N).T)
+    bt = O.gemm_epilogue(c.A, Bt, c.bias, None, M, N, K, dtype, "BIAS", True, False)
+    assert np.array_equal(bt.out, b.out)
+    # DRELU_BGRAD: all-ones mask == DEFAULT and bgrad = column sums of acc
+    ones = wl.const_mask(M, N, True)
+    g1 = O.gemm_epilogue(c.A, c.B, None, ones, M, N, K, dtype, "DRELU_BGRAD", False, False)
+    assert np.array_equal(g1.out, d.out)
+    colsum = (O.decode(c.A, dtype).reshape(M, K) @ O.decode(c.B, dtype).reshape(K, N)).sum(0)
+    assert np.allclose(g1.bgrad, colsum.astype(np.float32), rtol=1e-6, atol=1e-6)
+    # all-zeros mask -> dZ = 0 and bgrad = 0 exactly
+    z0 = O.gemm_epilogue(c.A, c.B, None, wl.const_mask(M, N, False), M, N, K, dtype,
+                         "DRELU_BGRAD", False, False)
+    assert np.all(O.decode(z0.out, dtype) == 0) and np.all(z0.bgrad == 0)
+    # bgrad equals the column sum of the masked gradient
+    rm = wl.random_mask(M, N, 5)
+    g = O.gemm_epilogue(c.A, c.B, None, rm, M, N, K, dtype, "DRELU_BGRAD", False, False)
+    mm = O.unpack_mask(rm, N)
+    acc = O.decode(c.A, dtype).reshape(M, K) @ O.decode(c.B, dtype).reshape(K, N)
+    assert np.allclose(g.bgrad, np.where(mm, acc, 0).sum(0), rtol=1e-6, atol=1e-6)
+
+
+def test_identity_b():
+    """B = I: y = round(A + bias)."""
+    M, K = 10, 24
+    A = wl.normal((M, K), 4, 1.0)
+    bias = wl.normal((M,), 5, 1.0)
+    eye = np.eye(K).astype(np.float16).view(np.uint16)
+    r = O.gemm_epilogue(A, eye, bias, None, M, K, K, "f16", "BIAS", False, False)
+    want = (O.decode_f16(A) + O.decode_f16(bias)[:, None]).astype(np.float16).view(np.uint16)
+    assert np.array_equal(r.out, want)
+
+
+def test_mask_pack_roundtrip_and_padding():
+    rng = np.random.default_rng(0)
+    for n in (1, 31, 32, 33, 100, 128, 129):
+        bits = rng.random((5, n)) < 0.5
+        w = O.pack_mask(bits)
+        assert w.shape == (5, O.aux_ld_words(n))
+        assert O.aux_ld_words(n) % 4 == 0
+        assert np.array_equal(O.unpack_mask(w, n), bits)
+        allbits = O.unpack_mask(w, w.shape[1] * 32)
+        assert not allbits[:, n:].any()
+    # bit order: column j is bit (j & 31) of word j >> 5
+    b = np.zeros((1, 64), bool); b[0, 33] = True
+    assert O.pack_mask(b)[0, 1] == 2 and O.pack_mask(b)[0, 0] == 0
+
+
+def test_ffn_chain_composes():
+    tok, H, I = 3, 16, 24
+    x = wl.normal((tok, H), 1)
+    W1 = wl.normal((I, H), 2, 0.25); b1 = wl.normal((I,), 3, 0.1)
+    W2 = wl.normal((H, I), 4, 0.2); b2 = wl.normal((H,), 5, 0.1)
+    h, y = O.ffn_block(x, W1, b1, W2, b2, tok, H, I, "f16")
+    hb, _, _ = brute.fused(x.ravel().tolist(), W1.ravel().tolist(), b1.tolist(), None,
+                           tok, I, H, "f16", "GELU_BIAS", True, True)
+    assert h.out.tolist() == hb
+    yb, _, _ = brute.fused(np.array(hb, np.uint16).ravel().tolist(), W2.ravel().tolist(),
+                           b2.tolist(), None, tok, H, I, "f16", "BIAS", True, True)
+    assert y.out.tolist() == yb

@@ -1,0 +1,310 @@
+// Unfused baseline: the separate elementwise kernels that follow a plain
+// GEMM when the epilogue is not fused.  Each one reads the GEMM result from
+// HBM and writes it back, which is the traffic and the extra launches the
+// fused kernel removes ("Fusing bias addition with matrix multiplication
+// using nvmath-python", paragraph 1; ops-nn MatMul fusion article, section
+// "Level 1: basic fusion", the three-step native flow).  They are written
+// to stream at HBM speed (128-bit accesses, grid-stride loops) so that the
+// measured fusion gain is against a competent baseline.
+//
+// Also the fp32 zero-fill used before the bias-gradient reduction (a kernel,
+// not hipMemsetAsync, so that a captured stream replays it correctly).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_mfma.hpp"
+#include "kernels.h"
+
+namespace gemmepi {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+inline int grid_for(int64_t work, int64_t per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack8(u32x4 w, float (&f)[8]) {
+  const T* h = reinterpret_cast<const T*>(&w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = to_f32(h[e]);
+}
+template <typename T>
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+  u32x4 w;
+  T* h = reinterpret_cast<T*>(&w);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = from_f32<T>(f[e]);
+  return w;
+}
+
+// out = round(out + bias); 8 elements per thread when rows are 16 B aligned.
+template <typename T>
+__global__ void bias_add_kernel(T* out, const T* bias, int M, int N, int ldo, int per_col, int vec) {
+  const int cpr = vec ? N / 8 : N;
+  const int64_t total = (int64_t)M * cpr;
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = c / cpr;
+    const int j = (int)(c - m * cpr);
+    if (vec) {
+      const int n = j * 8;
+      u32x4* ptr = (u32x4*)(out + m * ldo + n);
+      float f[8];
+      unpack8<T>(*ptr, f);
+      const float bm = per_col ? 0.0f : to_f32(bias[m]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] += per_col ? to_f32(bias[n + e]) : bm;
+      *ptr = pack8<T>(f);
+    } else {
+      T* q = out + m * ldo + j;
+      *q = from_f32<T>(to_f32(*q) + to_f32(per_col ? bias[j] : bias[m]));
+    }
+  }
+}
+
+// In-place ReLU or GELU, no mask.
+template <typename T>
+__global__ void act_kernel(T* out, int M, int N, int ldo, int epi, int vec) {
+  const int cpr = vec ? N / 8 : N;
+  const int64_t total = (int64_t)M * cpr;
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = c / cpr;
+    const int j = (int)(c - m * cpr);
+    if (vec) {
+      u32x4* ptr = (u32x4*)(out + m * ldo + j * 8);
+      float f[8];
+      unpack8<T>(*ptr, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] = (epi == EPI_GELU_BIAS) ? gelu_erf(f[e]) : (f[e] > 0.0f ? f[e] : 0.0f);
+      *ptr = pack8<T>(f);
+    } else {
+      T* q = out + m * ldo + j;
+      const float z = to_f32(*q);
+      *q = from_f32<T>((epi == EPI_GELU_BIAS) ? gelu_erf(z) : (z > 0.0f ? z : 0.0f));
+    }
+  }
+}
+
+// In-place ReLU that also writes the packed mask.  Four consecutive lanes
+// own the 32 columns of one mask word (8 each) and OR their bytes together;
+// every row is padded to aux_ld words so groups never straddle rows.
+template <typename T>
+__global__ void relu_mask_kernel(T* out, uint32_t* aux, int M, int N, int ldo, int aux_ld,
+                                 int aux_words, int vec) {
+  const int64_t slots_per_row = (int64_t)aux_words * 4;
+  const int64_t total = (int64_t)M * slots_per_row;
+  for (int64_t s = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; s < total;
+       s += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = s / slots_per_row;
+    const int rem = (int)(s - m * slots_per_row);
+    const int word = rem >> 2, sub = rem & 3;
+    const int n = word * 32 + sub * 8;
+    uint32_t bits = 0;
+    if (vec && n + 8 <= N) {
+      u32x4* ptr = (u32x4*)(out + m * ldo + n);
+      float f[8];
+      unpack8<T>(*ptr, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bits |= (f[e] > 0.0f ? 1u : 0u) << e;
+        f[e] = f[e] > 0.0f ? f[e] : 0.0f;
+      }
+      *ptr = pack8<T>(f);
+    } else {
+      for (int e = 0; e < 8 && n + e < N; ++e) {
+        T* q = out + m * ldo + n + e;
+        const float z = to_f32(*q);
+        bits |= (z > 0.0f ? 1u : 0u) << e;
+        *q = from_f32<T>(z > 0.0f ? z : 0.0f);
+      }
+    }
+    uint32_t w = bits << (sub * 8);
+    w |= __shfl_xor(w, 1);
+    w |= __shfl_xor(w, 2);
+    if (sub == 0) {
+      uint32_t* row = aux + m * aux_ld;
+      row[word] = w;
+      if (word == aux_words - 1)
+        for (int x = aux_words; x < aux_ld; ++x) row[x] = 0u;
+    }
+  }
+}
+
+// dZ = mask ? G : 0, in place.
+template <typename T>
+__global__ void mask_apply_kernel(T* out, const uint32_t* aux, int M, int N, int ldo, int aux_ld,
+                                  int vec) {
+  const int cpr = vec ? N / 8 : N;
+  const int64_t total = (int64_t)M * cpr;
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = c / cpr;
+    const int j = (int)(c - m * cpr);
+    if (vec) {
+      const int n = j * 8;
+      const uint32_t w = aux[m * aux_ld + (n >> 5)] >> (n & 31);
+      u32x4* ptr = (u32x4*)(out + m * ldo + n);
+      float f[8];
+      unpack8<T>(*ptr, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = ((w >> e) & 1u) ? f[e] : 0.0f;
+      *ptr = pack8<T>(f);
+    } else {
+      const uint32_t w = aux[m * aux_ld + (j >> 5)] >> (j & 31);
+      T* q = out + m * ldo + j;
+      if (!(w & 1u)) *q = from_f32<T>(0.0f);
+    }
+  }
+}
+
+// bgrad[n] += sum over a block of rows of dz[m][n] (fp32), bgrad pre-zeroed.
+// Block = 4 waves; each thread sums 8 columns over the wave's row slice,
+// the 4 slices are combined in LDS, then one atomic per column per block.
+constexpr int kColsumRows = 256;  // rows per block (64 per wave)
+
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_kernel(const T* dz, float* bgrad, int M, int N,
+                                                     int ldo) {
+  __shared__ float part[4][64 * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = (blockIdx.x * 64 + lane) * 8;
+  const int m_beg = blockIdx.y * kColsumRows + wave * (kColsumRows / 4);
+  const int m_end = min(M, m_beg + kColsumRows / 4);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (n < N) {
+    int m = m_beg;
+    for (; m + 8 <= m_end; m += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *(const u32x4*)(dz + (int64_t)(m + u) * ldo + n);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float f[8];
+        unpack8<T>(v[u], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += f[e];
+      }
+    }
+    for (; m < m_end; ++m) {
+      float f[8];
+      unpack8<T>(*(const u32x4*)(dz + (int64_t)m * ldo + n), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += f[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[wave][lane * 8 + e] = acc[e];
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int col = blockIdx.x * 512 + i;
+    if (col < N) unsafeAtomicAdd(&bgrad[col], part[0][i] + part[1][i] + part[2][i] + part[3][i]);
+  }
+}
+
+// Scalar fallback for rows that are not 16 B aligned: one thread per column.
+template <typename T>
+__global__ void colsum_scalar_kernel(const T* dz, float* bgrad, int M, int N, int ldo) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.0f;
+  for (int m = 0; m < M; ++m) s += to_f32(dz[(int64_t)m * ldo + n]);
+  bgrad[n] = s;
+}
+
+}  // namespace
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+static inline int vec_ok(const void* p, int N, int ldo) {
+  return ((uintptr_t)p % 16 == 0) && (N % 8 == 0) && (ldo % 8 == 0);
+}
+
+hipError_t launch_bias_add(int dtype, void* out, const void* bias, int M, int N, int ldo,
+                           int per_col, hipStream_t s) {
+  const int vec = vec_ok(out, N, ldo);
+  const int64_t work = (int64_t)M * (vec ? N / 8 : N);
+  if (dtype == DT_F16)
+    hipLaunchKernelGGL(bias_add_kernel<_Float16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0,
+                       s, (_Float16*)out, (const _Float16*)bias, M, N, ldo, per_col, vec);
+  else
+    hipLaunchKernelGGL(bias_add_kernel<__bf16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0, s,
+                       (__bf16*)out, (const __bf16*)bias, M, N, ldo, per_col, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_activation(int dtype, int epi, void* out, uint32_t* aux, int M, int N, int ldo,
+                             int aux_ld, hipStream_t s) {
+  const int vec = vec_ok(out, N, ldo);
+  if (epi == EPI_RELU_AUX_BIAS) {
+    const int aux_words = (N + 31) / 32;
+    const int64_t work = (int64_t)M * aux_words * 4;
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(relu_mask_kernel<_Float16>, dim3(grid_for(work, kThreads)), dim3(kThreads),
+                         0, s, (_Float16*)out, aux, M, N, ldo, aux_ld, aux_words, vec);
+    else
+      hipLaunchKernelGGL(relu_mask_kernel<__bf16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0,
+                         s, (__bf16*)out, aux, M, N, ldo, aux_ld, aux_words, vec);
+  } else {
+    const int64_t work = (int64_t)M * (vec ? N / 8 : N);
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(act_kernel<_Float16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0, s,
+                         (_Float16*)out, M, N, ldo, epi, vec);
+    else
+      hipLaunchKernelGGL(act_kernel<__bf16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0, s,
+                         (__bf16*)out, M, N, ldo, epi, vec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_apply(int dtype, void* out, const uint32_t* aux, int M, int N, int ldo,
+                             int aux_ld, hipStream_t s) {
+  const int vec = vec_ok(out, N, ldo);
+  const int64_t work = (int64_t)M * (vec ? N / 8 : N);
+  if (dtype == DT_F16)
+    hipLaunchKernelGGL(mask_apply_kernel<_Float16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0,
+                       s, (_Float16*)out, aux, M, N, ldo, aux_ld, vec);
+  else
+    hipLaunchKernelGGL(mask_apply_kernel<__bf16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0,
+                       s, (__bf16*)out, aux, M, N, ldo, aux_ld, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(int dtype, const void* dz, float* bgrad, int M, int N, int ldo,
+                         hipStream_t s) {
+  if (vec_ok(dz, N, ldo)) {
+    dim3 grid((N / 8 + 63) / 64, (M + kColsumRows - 1) / kColsumRows);
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(colsum_kernel<_Float16>, grid, dim3(256), 0, s, (const _Float16*)dz, bgrad, M,
+                         N, ldo);
+    else
+      hipLaunchKernelGGL(colsum_kernel<__bf16>, grid, dim3(256), 0, s, (const __bf16*)dz, bgrad, M, N,
+                         ldo);
+  } else {
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL(colsum_scalar_kernel<_Float16>, dim3((N + 255) / 256), dim3(256), 0, s,
+                         (const _Float16*)dz, bgrad, M, N, ldo);
+    else
+      hipLaunchKernelGGL(colsum_scalar_kernel<__bf16>, dim3((N + 255) / 256), dim3(256), 0, s,
+                         (const __bf16*)dz, bgrad, M, N, ldo);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gemmepi

@@ -1,0 +1,11 @@
+// Tiled MFMA GEMM instantiations: f16 inputs, B stored [N,K] (K contiguous).
+// One file per (dtype, B layout) so the tile variants compile in parallel.
+#include "gemm_mfma.hpp"
+
+namespace gemmepi {
+
+hipError_t launch_gemm_f16_bt(int tile, const GemmArgs& a, hipStream_t s) {
+  return launch_by_tile<_Float16, true>(tile, a, s);
+}
+
+}  // namespace gemmepi

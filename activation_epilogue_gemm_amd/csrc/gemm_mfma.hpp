@@ -1,0 +1,498 @@
+// Tiled MFMA GEMM with an in-register epilogue, for gfx950 (MI355X).
+//
+//   out[M,N] = epilogue(A[M,K] . B + bias)
+//
+// The GEMM result never leaves the chip before the epilogue: bias add,
+// activation, mask packing and bias-gradient reduction are applied to the
+// fp32 accumulators, then each output element is rounded and written once.
+// This is the fused sequence of the pages (the GEMM result stays in
+// registers / on-chip memory and is combined with the bias there before a
+// single write-back: "Fusing bias addition with matrix multiplication using
+// nvmath-python", paragraph 2; ops-nn MatMul fusion article, section
+// "Level 1: basic fusion"), designed here for CDNA4 rather than taken from
+// those pages' hardware.
+//
+// Structure of one workgroup (WM x WN wavefronts of 64 lanes):
+//   * the workgroup owns a BM x BN output tile; wave (wm, wn) owns a
+//     (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles;
+//   * K is walked in slabs of BK.  Each slab of A [BM x BK] and of B is
+//     fetched with 128-bit buffer loads that write straight into LDS (no
+//     register staging), into one of two stage buffers, while the MFMAs
+//     consume the other stage; one barrier per slab.  Out-of-range rows,
+//     columns and k read as zero through the buffer descriptor's range
+//     check.  The two stages are separate LDS objects and the slab loop is
+//     unrolled by two, so the compiler can see that the loads in flight
+//     never alias the stage being read and does not wait for them;
+//   * LDS rows are XOR-swizzled in 16-byte units so that the 128-bit
+//     fragment reads (and the 64-bit transposing reads of a row-major [K,N]
+//     B) hit distinct banks of the 64-bank LDS;
+//   * v_mfma_f32_32x32x16_{f16,bf16}: exact products, fp32 accumulation.
+//     The B fragment is passed as the instruction's first operand and the A
+//     fragment as its second, so the accumulator holds the transposed tile:
+//     lane l, element r of a 32x32 tile is
+//         row m = l % 32,   column n = 8*(r/4) + 4*(l/32) + (r%4),
+//     i.e. each lane owns one output row and 4 runs of 4 consecutive
+//     columns, which become 8-byte stores.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace gemmepi {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define GEMMEPI_LDS __attribute__((address_space(3)))
+
+// Out-of-range voffset: larger than the descriptor's record count, so the
+// buffer load returns zeros.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kNumRecords = 0x7FFFFFFF;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  // gfx9 family descriptor word 3 (no swizzle, 32-bit data format).
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, kNumRecords, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane L's data lands at
+// LDS byte address lds_addr + 16 L (lds_addr must be wave-uniform; it goes
+// to M0).  Written as inline assembly on purpose: the compiler then does not
+// see an LDS write in flight, and does not make every later LDS read wait
+// for it (it cannot prove that the transposing reads of the other stage do
+// not alias it).  The caller orders these writes with wait_loads() and a
+// barrier before any wave reads the stage.
+__device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr,
+                                                  uint32_t off) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(off), "s"(r), "s"(lds_addr)
+               : "memory");
+}
+
+// Wait until every vector memory operation of this wave (including the LDS
+// writes of buffer->LDS loads) has completed.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const GEMMEPI_LDS void*)p;
+}
+
+template <typename T> struct Frag;
+template <> struct Frag<_Float16> { using type = f16x8; };
+template <> struct Frag<__bf16> { using type = bf16x8; };
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 4 consecutive-k values of one column from a row-major [K,N] LDS tile:
+// within each group of 16 lanes, lane (4*h + q) points at row h, columns
+// 4q..4q+3 of a 4 x 16 block; after the transposing read lane i holds
+// column i of the block (rows 0..3).
+__device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p, _Float16) {
+  fp16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((GEMMEPI_LDS fp16x4_t*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x2 lds_read_tr(const uint8_t* p, __bf16) {
+  bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GEMMEPI_LDS bf16x4_t*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
+
+// Two fp32 values -> one 32-bit word of two 16-bit values (round to nearest
+// even; the low half is `a`).
+__device__ __forceinline__ uint32_t pack2(float a, float b, _Float16) {
+  f16x2 h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b, __bf16) {
+  bf16x2 h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Exact (erf) GELU: gelu(z) = z Phi(z) = 0.5 z (1 + erf(z / sqrt 2)).
+// erf is evaluated with Abramowitz & Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (|error| <= 1.5e-7 for x >= 0):
+//   erf(x) = 1 - q,  q = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x).
+// With x = |z| / sqrt 2 this gives 1 + erf(z/sqrt 2) = 2 - q for z >= 0 and
+// q for z < 0, so the negative branch keeps full relative accuracy.
+// Branch-free, about a dozen VALU operations.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float x = fabsf(z) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  // exp(-x^2) = 2^(-x^2 log2 e)
+  const float q = poly * __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
+  const float one_plus_erf = z >= 0.0f ? 2.0f - q : q;
+  return 0.5f * z * one_plus_erf;
+}
+
+// blockIdx -> output tile.  With xcd_remap, the hardware's round-robin of
+// consecutive workgroups over the 8 XCDs is undone so that each XCD (with
+// its own L2) walks a contiguous run of the tile order; the tile order is
+// grouped by `group_m` tile rows so that concurrently running tiles share
+// A row panels and B column panels.
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
+  int bid = blockIdx.x;
+  const int nb = gridDim.x;
+  if (p.xcd_remap) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
+  const int per_group = p.group_m * p.tiles_n;
+  const int g = bid / per_group;
+  const int first_m = g * p.group_m;
+  const int gsz = min(p.tiles_m - first_m, p.group_m);
+  const int r = bid - g * per_group;
+  tm = first_m + r % gsz;
+  tn = r / gsz;
+}
+
+template <int BM, int BN, int BK, int WM, int WN>
+struct GemmTile {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int NW = WM * WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int KCH = BK / 8;                 // 16 B chunks per K-contiguous row
+  static constexpr int NCH = BN / 8;                 // 16 B chunks per N-contiguous row
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_CH = A_BYTES / (NT * 16);   // 1 KiB load blocks per wave (A)
+  static constexpr int B_CH = B_BYTES / (NT * 16);   // 1 KiB load blocks per wave (B)
+  static constexpr int A_RPB = 1024 / (BK * 2);      // K-contiguous rows per 1 KiB block
+  static constexpr int B_RPB = 1024 / (BN * 2);      // N-contiguous rows per 1 KiB block
+  // rows sharing one 256-byte bank line
+  static constexpr int RPK = (BK * 2 >= 256) ? 1 : 256 / (BK * 2);
+  static constexpr int RPN = (BN * 2 >= 256) ? 1 : 256 / (BN * 2);
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+  static_assert(BK % 16 == 0 && BK >= 32, "BK");
+  static_assert(A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "load split");
+  static_assert(64 % KCH == 0 && 64 % NCH == 0 && BN * 2 <= 1024, "load split");
+  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+  static_assert(WM * BN * 4 <= STAGE, "bias-gradient scratch");
+
+  // 16 B-chunk swizzle of a K-contiguous row r (A, or B stored [N,K])
+  static __device__ __forceinline__ int swz_k(int r) { return (r / RPK) % KCH; }
+  // 16 B-chunk swizzle of an N-contiguous row kr (B stored [K,N])
+  static __device__ __forceinline__ int swz_n(int kr) { return (4 * (kr / RPN)) % NCH; }
+};
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool BT>
+__global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p) {
+  using G = GemmTile<BM, BN, BK, WM, WN>;
+  using V8 = typename Frag<T>::type;
+  constexpr int NT = G::NT, NW = G::NW, WTM = G::WTM, WTN = G::WTN, FM = G::FM, FN = G::FN;
+  constexpr int KCH = G::KCH, NCH = G::NCH, A_CH = G::A_CH, B_CH = G::B_CH;
+
+  __shared__ __attribute__((aligned(1024))) uint8_t stage0[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t stage1[G::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int M = p.M, N = p.N, K = p.K;
+
+  // ---- slab loads: 128-bit buffer loads straight into LDS ----------------
+  // Each load instruction of a wave fills one contiguous 1 KiB block of an
+  // LDS stage (lane L -> bytes 16L..16L+15).  The swizzled layout is made by
+  // choosing which global chunk each lane fetches: the lane that owns LDS
+  // chunk slot `phys` of row r fetches logical chunk phys ^ swizzle(r).
+  uint32_t a_off[A_CH];
+  int a_k[A_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int blk = i * NW + wave;
+    const int r = blk * G::A_RPB + lane / KCH;
+    const int kc = (lane % KCH) ^ G::swz_k(r);
+    a_off[i] = (m0 + r < M) ? (uint32_t)((r * p.lda + kc * 8) * 2) : kOOB;
+    a_k[i] = kc * 8;
+  }
+  uint32_t b_off[B_CH];
+  int b_k[B_CH];
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int blk = i * NW + wave;
+    if constexpr (BT) {  // B stored [N,K]: rows are n
+      const int r = blk * G::A_RPB + lane / KCH;
+      const int kc = (lane % KCH) ^ G::swz_k(r);
+      b_off[i] = (n0 + r < N) ? (uint32_t)((r * p.ldb + kc * 8) * 2) : kOOB;
+      b_k[i] = kc * 8;
+    } else {             // B stored [K,N]: rows are k
+      const int kr = blk * G::B_RPB + lane / NCH;
+      const int nc = (lane % NCH) ^ G::swz_n(kr);
+      b_off[i] = (n0 + nc * 8 < N) ? (uint32_t)((kr * p.ldb + nc * 8) * 2) : kOOB;
+      b_k[i] = kr;
+    }
+  }
+
+  const uint8_t* Abase = (const uint8_t*)p.A + (size_t)m0 * p.lda * 2;
+  const uint8_t* Bbase = BT ? (const uint8_t*)p.B + (size_t)n0 * p.ldb * 2
+                            : (const uint8_t*)p.B + (size_t)n0 * 2;
+  const int KT = (K + BK - 1) / BK;
+  const bool ktail = (K % BK) != 0;
+
+  auto issue = [&](int kt, uint8_t* st) {
+    const uint32_t st_addr = __builtin_amdgcn_readfirstlane(lds_addr_of(st));
+    const int k0 = kt * BK;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (size_t)k0 * 2);
+    const __amdgpu_buffer_rsrc_t rB =
+        BT ? make_rsrc(Bbase + (size_t)k0 * 2) : make_rsrc(Bbase + (size_t)k0 * p.ldb * 2);
+    const bool last = ktail && (kt == KT - 1);
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i) {
+      uint32_t off = a_off[i];
+      if (last && k0 + a_k[i] >= K) off = kOOB;
+      buffer_load16_lds(rA, st_addr + (i * NW + wave) * 1024, off);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CH; ++i) {
+      uint32_t off = b_off[i];
+      if (last && k0 + b_k[i] >= K) off = kOOB;
+      buffer_load16_lds(rB, st_addr + G::A_BYTES + (i * NW + wave) * 1024, off);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int lrow = lane & 31;   // row (A) / column (B) within a 32x32 MFMA tile
+  const int khalf = lane >> 5;  // which 8-wide k group of a 16-wide step
+
+  auto compute = [&](const uint8_t* sA) {
+    const uint8_t* sB = sA + G::A_BYTES;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      V8 af[FM], bf[FN];
+      const int kc = ks * 2 + khalf;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int r = wm * WTM + fm * 32 + lrow;
+        af[fm] = *(const V8*)(sA + r * BK * 2 + ((kc ^ G::swz_k(r)) << 4));
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        if constexpr (BT) {
+          const int r = wn * WTN + fn * 32 + lrow;
+          bf[fn] = *(const V8*)(sB + r * BK * 2 + ((kc ^ G::swz_k(r)) << 4));
+        } else {
+          // two transposing reads: k = ks*16 + 8*(lane/32) + {0..3, 4..7}
+          const int g = lane >> 4, i = lane & 15;
+          const int ncol = wn * WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
+          const int nc = ncol >> 3, nb = (ncol & 7) * 2;
+          const int kr0 = ks * 16 + (g >> 1) * 8 + (i >> 2);
+          const int kr1 = kr0 + 4;
+          const u32x2 lo = lds_read_tr(sB + kr0 * BN * 2 + ((nc ^ G::swz_n(kr0)) << 4) + nb, T{});
+          const u32x2 hi = lds_read_tr(sB + kr1 * BN * 2 + ((nc ^ G::swz_n(kr1)) << 4) + nb, T{});
+          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+          bf[fn] = __builtin_bit_cast(V8, w);
+        }
+      }
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma32(bf[fn], af[fm], acc[fm][fn]);
+    }
+  };
+
+  issue(0, stage0);
+  wait_loads();
+  __syncthreads();
+  int kt = 0;
+  for (; kt + 2 <= KT; kt += 2) {  // two slabs per trip: stage0 then stage1
+    issue(kt + 1, stage1);
+    compute(stage0);
+    wait_loads();
+    __syncthreads();
+    if (kt + 2 < KT) issue(kt + 2, stage0);
+    compute(stage1);
+    wait_loads();
+    __syncthreads();
+  }
+  if (kt < KT) compute(stage0);  // odd slab count: the last slab is in stage0
+
+  // ---- epilogue on the accumulators -----------------------------------------
+  // lane owns row m = wrow0 + 32 fm + lrow and, in tile (fm, fn), columns
+  // cgrp + 8 g + {0,1,2,3} for g = 0..3 (elements r = 4 g + e).
+  const int epi = p.epi;
+  const int wrow0 = m0 + wm * WTM;
+  const int wcol0 = n0 + wn * WTN;
+  const size_t ldo = (size_t)p.ldo;
+  const bool vec_store = (p.ldo & 3) == 0;  // 8-byte aligned 4-column groups
+
+  auto store_tile = [&](int m, int cgrp, const float (&y)[16]) {
+    if (m >= M) return;
+    T* orow = (T*)p.out + (size_t)m * ldo;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = cgrp + 8 * g;
+      if (vec_store && c + 3 < N) {
+        u32x2 w = {pack2(y[4 * g], y[4 * g + 1], T{}), pack2(y[4 * g + 2], y[4 * g + 3], T{})};
+        *(u32x2*)(orow + c) = w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < N) orow[c + e] = from_f32<T>(y[4 * g + e]);
+      }
+    }
+  };
+
+  if (epi == EPI_DRELU_BGRAD) {
+    // dZ = mask ? acc : 0; bgrad[n] += sum over this tile's rows of dZ
+    float cs[FN][16];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cs[fn][r] = 0.0f;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int m = wrow0 + fm * 32 + lrow;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int cbase = wcol0 + fn * 32;
+        const uint32_t mw = (m < M && cbase < N)
+                                ? p.aux[(size_t)m * p.aux_ld + (cbase >> 5)] >> (4 * khalf)
+                                : 0u;
+        float y[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int bit = 8 * (r >> 2) + (r & 3);
+          y[r] = ((mw >> bit) & 1u) ? acc[fm][fn][r] : 0.0f;
+          cs[fn][r] += y[r];
+        }
+        store_tile(m, cbase + 4 * khalf, y);
+      }
+    }
+    // sum over the 32 rows held by the lanes with the same khalf
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = cs[fn][r];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        cs[fn][r] = v;
+      }
+    float* red = (float*)stage0;  // [WM][BN] column sums per wave row
+    if (lrow == 0) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          red[wm * BN + wn * WTN + fn * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3)] = cs[fn][r];
+    }
+    __syncthreads();
+    for (int c = tid; c < BN; c += NT) {
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WM; ++w) s += red[w * BN + c];
+      if (n0 + c < N) unsafeAtomicAdd(&p.bgrad[n0 + c], s);
+    }
+    return;
+  }
+
+  const bool has_bias = epi != EPI_DEFAULT;
+  const bool per_col = p.bias_per_col != 0;
+  const T* bias = (const T*)p.bias;
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int m = wrow0 + fm * 32 + lrow;
+    const float brow = (has_bias && !per_col && m < M) ? to_f32(bias[m]) : 0.0f;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int cbase = wcol0 + fn * 32;
+      const int cgrp = cbase + 4 * khalf;
+      float y[16];
+      uint32_t bits = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = cgrp + 8 * (r >> 2) + (r & 3);
+        float b = brow;
+        if (has_bias && per_col) b = c < N ? to_f32(bias[c]) : 0.0f;
+        const float z = acc[fm][fn][r] + b;
+        if (epi == EPI_GELU_BIAS) {
+          y[r] = gelu_erf(z);
+        } else if (epi == EPI_RELU_BIAS || epi == EPI_RELU_AUX_BIAS) {
+          y[r] = z > 0.0f ? z : 0.0f;
+        } else {
+          y[r] = z;
+        }
+        if (epi == EPI_RELU_AUX_BIAS && z > 0.0f && c < N)
+          bits |= 1u << (8 * (r >> 2) + 4 * khalf + (r & 3));
+      }
+      store_tile(m, cgrp, y);
+      if (epi == EPI_RELU_AUX_BIAS) {
+        // lanes l and l+32 hold complementary halves of row m's word
+        bits |= __shfl_xor(bits, 32);
+        if (khalf == 0 && m < M && cbase < N) {
+          uint32_t* mrow = p.aux + (size_t)m * p.aux_ld;
+          const int word = cbase >> 5;
+          mrow[word] = bits;
+          if (word == p.aux_words - 1)
+            for (int w = p.aux_words; w < p.aux_ld; ++w) mrow[w] = 0u;
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool BT>
+hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
+  const int blocks = a.tiles_m * a.tiles_n;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, BT>), dim3(blocks), dim3(WM * WN * 64), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+// The tile table: must match kTiles in gemmepi_api.cpp.
+template <typename T, bool BT>
+hipError_t launch_by_tile(int tile, const GemmArgs& a, hipStream_t s) {
+  switch (tile) {
+    case 0: return launch_tile<T, 256, 256, 64, 2, 2, BT>(a, s);
+    case 1: return launch_tile<T, 256, 256, 64, 2, 4, BT>(a, s);
+    case 2: return launch_tile<T, 256, 128, 64, 2, 2, BT>(a, s);
+    case 3: return launch_tile<T, 128, 128, 64, 2, 2, BT>(a, s);
+    case 4: return launch_tile<T, 128, 64, 64, 2, 2, BT>(a, s);
+    case 5: return launch_tile<T, 64, 64, 64, 2, 2, BT>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace gemmepi

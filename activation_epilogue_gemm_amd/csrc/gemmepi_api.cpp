@@ -1,0 +1,441 @@
+// C ABI of libgemmepi: argument validation, the plan cache and the dispatch
+// of the fused and unfused paths.  Host code only; the kernels live in the
+// .hip files.
+//
+// The plan/execute split follows the pages' stateful Matmul object: a
+// lazy, checks-only construction, a costly planning step that picks the
+// algorithm and kernel configuration for the shape and is cached so its
+// cost is amortised, then cheap executions ("Fusing bias addition with
+// matrix multiplication using nvmath-python", paragraphs 3 and 5;
+// "nvmath-python cuBLASLt bias fusion guide", section "Advanced techniques
+// and engineering practice").  Here planning is a deterministic shape ->
+// tile table lookup, done on the host without touching the GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "gemmepi.h"
+#include "kernels.h"
+
+namespace gemmepi {
+
+const TileCfg kTiles[kNumTiles] = {
+    {256, 256, 64, 2, 2, "256x256x64_w2x2"}, {256, 256, 64, 2, 4, "256x256x64_w2x4"},
+    {256, 128, 64, 2, 2, "256x128x64_w2x2"}, {128, 128, 64, 2, 2, "128x128x64_w2x2"},
+    {128, 64, 64, 2, 2, "128x64x64_w2x2"},   {64, 64, 64, 2, 2, "64x64x64_w2x2"},
+};
+
+// Relative throughput of one CU on a full tile of each configuration, and
+// how many of its workgroups fit on one CU (LDS and registers).  Used only
+// to rank tiles for a shape: est = rounds * occupancy * BM * BN / eff.
+static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.55, 0.40};
+static const int kTileOcc[kNumTiles] = {1, 1, 1, 2, 3, 4};
+constexpr int kNumCU = 256;
+
+hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s) {
+  if (dtype == DT_F16)
+    return b_trans ? launch_gemm_f16_bt(tile, a, s) : launch_gemm_f16_bn(tile, a, s);
+  return b_trans ? launch_gemm_bf16_bt(tile, a, s) : launch_gemm_bf16_bn(tile, a, s);
+}
+
+}  // namespace gemmepi
+
+using namespace gemmepi;
+
+enum PlanPath { PATH_GEMM = 0, PATH_DECODE = 1 };
+
+struct gemmepi_plan_s {
+  int64_t M, N, K;
+  int dtype, epi;
+  uint32_t flags;
+  int tile_req;
+  int path;
+  int tile;
+  int tiles_m, tiles_n, group_m, xcd_remap;
+  int k_per_wave;
+  int refs;
+  std::string info;
+};
+
+namespace {
+
+using Key = std::tuple<int64_t, int64_t, int64_t, int, int, uint32_t, int>;
+
+std::mutex g_mu;
+std::map<Key, gemmepi_plan_s*>& cache() {
+  static std::map<Key, gemmepi_plan_s*> c;
+  return c;
+}
+thread_local std::string g_err;
+
+gemmepi_status_t fail(gemmepi_status_t s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+constexpr uint32_t kAllFlags = GEMMEPI_FLAG_B_TRANS | GEMMEPI_FLAG_BIAS_PER_COL |
+                               GEMMEPI_FLAG_UNFUSED | GEMMEPI_FLAG_VALIDATE |
+                               GEMMEPI_FLAG_NO_DECODE;
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+
+bool log_enabled() {
+  static int v = [] {
+    const char* e = getenv("GEMMEPI_LOG");
+    return (e && *e && *e != '0') ? 1 : 0;
+  }();
+  return v != 0;
+}
+
+int choose_tile(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  int best = 0;
+  double best_est = 0.0;
+  for (int t = 0; t < kNumTiles; ++t) {
+    const TileCfg& c = kTiles[t];
+    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const int64_t slots = (int64_t)kNumCU * kTileOcc[t];
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double est = (double)rounds * kTileOcc[t] * c.bm * c.bn / kTileEff[t];
+    if (t == 0 || est < best_est) {
+      best = t;
+      best_est = est;
+    }
+  }
+  return best;
+}
+
+void describe(gemmepi_plan_s* p) {
+  char buf[384];
+  static const char* epis[] = {"DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS",
+                               "DRELU_BGRAD"};
+  if (p->path == PATH_DECODE) {
+    snprintf(buf, sizeof(buf),
+             "path=decode M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x grid=%lld waves=8 "
+             "k_per_wave=%d%s",
+             (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
+             epis[p->epi], p->flags, (long long)((p->N + 15) / 16), p->k_per_wave,
+             (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
+  } else {
+    const TileCfg& c = kTiles[p->tile];
+    snprintf(buf, sizeof(buf),
+             "path=gemm M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x tile=%s tiles=%dx%d "
+             "group_m=%d xcd_remap=%d%s",
+             (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
+             epis[p->epi], p->flags, c.name, p->tiles_m, p->tiles_n, p->group_m, p->xcd_remap,
+             (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
+  }
+  p->info = buf;
+}
+
+// Lazily checked per device: the kernels are built for gfx950 only.
+gemmepi_status_t check_device() {
+  static int ok_dev[64] = {0};  // 0 unknown, 1 ok, -1 bad
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(GEMMEPI_ERR_DEVICE, "device index %d out of range", dev);
+  if (ok_dev[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(GEMMEPI_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    ok_dev[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    if (ok_dev[dev] < 0)
+      return fail(GEMMEPI_ERR_HIP, "device %d is %s; libgemmepi is built for gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  if (ok_dev[dev] < 0) return fail(GEMMEPI_ERR_HIP, "device %d is not gfx950", dev);
+  return GEMMEPI_OK;
+}
+
+gemmepi_status_t check_device_ptr(const void* p, const char* name) {
+  int dev = 0;
+  hipGetDevice(&dev);
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(GEMMEPI_ERR_DEVICE, "%s: not a HIP allocation (%s)", name, hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeDevice)
+    return fail(GEMMEPI_ERR_DEVICE, "%s: not device memory (type %d)", name, (int)attr.type);
+  if (attr.device != dev)
+    return fail(GEMMEPI_ERR_DEVICE, "%s: on device %d, current device is %d", name, attr.device,
+                dev);
+  return GEMMEPI_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
+                           gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags,
+                           int32_t tile_req) {
+  if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "plan: null output pointer");
+  *plan = nullptr;
+  if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "sizes must be in [1, 2^31-1]: M=%lld N=%lld K=%lld",
+                (long long)M, (long long)N, (long long)K);
+  if (dtype != GEMMEPI_F16 && dtype != GEMMEPI_BF16)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown dtype %d", (int)dtype);
+  if ((int)epi < GEMMEPI_EPI_DEFAULT || (int)epi > GEMMEPI_EPI_DRELU_BGRAD)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown epilogue %d", (int)epi);
+  if (flags & ~kAllFlags) return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown flag bits 0x%x", flags);
+  if (tile_req < -1 || tile_req >= kNumTiles)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown tile id %d", tile_req);
+  const bool bt = flags & GEMMEPI_FLAG_B_TRANS;
+  if (K % 8 != 0)
+    return fail(GEMMEPI_ERR_MISALIGNED, "K=%lld must be a multiple of 8", (long long)K);
+  if (!bt && N % 8 != 0)
+    return fail(GEMMEPI_ERR_MISALIGNED,
+                "N=%lld must be a multiple of 8 when B is stored [K,N] (no B_TRANS)",
+                (long long)N);
+  // 32-bit buffer offsets: a 256-row panel of A or of B must stay below 2 GiB
+  if (K * 2 * 256 >= 0x7FFFFFF0LL || (!bt && N * 2 * 64 >= 0x7FFFFFF0LL))
+    return fail(GEMMEPI_ERR_UNSUPPORTED, "leading dimension too large (K=%lld N=%lld)",
+                (long long)K, (long long)N);
+  if (M * N > (int64_t)1 << 40)
+    return fail(GEMMEPI_ERR_UNSUPPORTED, "output too large");
+
+  const Key key{M, N, K, (int)dtype, (int)epi, flags, tile_req};
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = cache().find(key);
+  if (it != cache().end()) {
+    it->second->refs += 1;
+    *plan = it->second;
+    return GEMMEPI_OK;
+  }
+  gemmepi_plan_s* p = new (std::nothrow) gemmepi_plan_s();
+  if (!p) return fail(GEMMEPI_ERR_NO_MEMORY, "plan allocation failed");
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->dtype = (int)dtype;
+  p->epi = (int)epi;
+  p->flags = flags;
+  p->tile_req = tile_req;
+  p->refs = 1;
+  const bool decode_epi = epi == GEMMEPI_EPI_DEFAULT || epi == GEMMEPI_EPI_BIAS ||
+                          epi == GEMMEPI_EPI_RELU_BIAS || epi == GEMMEPI_EPI_GELU_BIAS;
+  if (tile_req < 0 && !(flags & GEMMEPI_FLAG_NO_DECODE) && bt && M <= 16 && decode_epi) {
+    p->path = PATH_DECODE;
+    p->tile = -1;
+    const int64_t per = (K + 8 * 32 - 1) / (8 * 32) * 32;  // 8 waves, 32-wide steps
+    p->k_per_wave = (int)per;
+  } else {
+    p->path = PATH_GEMM;
+    p->tile = tile_req >= 0 ? tile_req : choose_tile(M, N, K);
+    const TileCfg& c = kTiles[p->tile];
+    p->tiles_m = (int)((M + c.bm - 1) / c.bm);
+    p->tiles_n = (int)((N + c.bn - 1) / c.bn);
+    p->group_m = p->tiles_m < 8 ? p->tiles_m : 8;
+    const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
+    p->xcd_remap = (tiles % 8 == 0 && tiles >= 64) ? 1 : 0;
+  }
+  describe(p);
+  if (log_enabled()) fprintf(stderr, "[gemmepi] plan %s\n", p->info.c_str());
+  cache()[key] = p;
+  *plan = p;
+  return GEMMEPI_OK;
+}
+
+bool plan_live(gemmepi_plan_t plan) {
+  for (auto& kv : cache())
+    if (kv.second == plan) return true;
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemmepi_status_t gemmepi_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
+                              gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags) {
+  return make_plan(plan, M, N, K, dtype, epi, flags, -1);
+}
+
+gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
+                                    gemmepi_dtype_t dtype, gemmepi_epilogue_t epi,
+                                    uint32_t flags, int32_t tile_id) {
+  return make_plan(plan, M, N, K, dtype, epi, flags, tile_id);
+}
+
+gemmepi_status_t gemmepi_plan_destroy(gemmepi_plan_t plan) {
+  if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "plan_destroy: null plan");
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto it = cache().begin(); it != cache().end(); ++it) {
+    if (it->second == plan) {
+      if (--plan->refs == 0) {
+        cache().erase(it);
+        delete plan;
+      }
+      return GEMMEPI_OK;
+    }
+  }
+  return fail(GEMMEPI_ERR_INVALID_VALUE, "plan_destroy: not a live plan");
+}
+
+gemmepi_status_t gemmepi_plan_info(gemmepi_plan_t plan, char* buf, size_t len) {
+  if (!plan || !buf || len == 0) return fail(GEMMEPI_ERR_INVALID_VALUE, "plan_info: bad argument");
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!plan_live(plan)) return fail(GEMMEPI_ERR_INVALID_VALUE, "plan_info: not a live plan");
+  snprintf(buf, len, "%s", plan->info.c_str());
+  return GEMMEPI_OK;
+}
+
+int32_t gemmepi_num_tiles(void) { return kNumTiles; }
+
+const char* gemmepi_tile_name(int32_t tile_id) {
+  if (tile_id < 0 || tile_id >= kNumTiles) return nullptr;
+  return kTiles[tile_id].name;
+}
+
+int64_t gemmepi_aux_ld_words(int64_t N) {
+  if (N < 1) return 0;
+  return ((N + 31) / 32 + 3) / 4 * 4;
+}
+
+size_t gemmepi_aux_bytes(int64_t M, int64_t N) {
+  if (M < 1 || N < 1) return 0;
+  return (size_t)M * (size_t)gemmepi_aux_ld_words(N) * 4u;
+}
+
+const char* gemmepi_status_string(gemmepi_status_t s) {
+  switch (s) {
+    case GEMMEPI_OK: return "GEMMEPI_OK";
+    case GEMMEPI_ERR_INVALID_VALUE: return "GEMMEPI_ERR_INVALID_VALUE";
+    case GEMMEPI_ERR_MISALIGNED: return "GEMMEPI_ERR_MISALIGNED";
+    case GEMMEPI_ERR_UNSUPPORTED: return "GEMMEPI_ERR_UNSUPPORTED";
+    case GEMMEPI_ERR_DEVICE: return "GEMMEPI_ERR_DEVICE";
+    case GEMMEPI_ERR_HIP: return "GEMMEPI_ERR_HIP";
+    case GEMMEPI_ERR_NO_MEMORY: return "GEMMEPI_ERR_NO_MEMORY";
+  }
+  return "unknown status";
+}
+
+const char* gemmepi_last_error(void) { return g_err.c_str(); }
+
+int32_t gemmepi_version(void) { return GEMMEPI_VERSION; }
+
+gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
+                                 void* aux, void* out, void* stream) {
+  if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: null plan");
+  // The plan is immutable after creation; callers keep it alive while they
+  // execute it, so no lock is taken on this path.
+  const gemmepi_plan_s& p = *plan;
+  const int epi = p.epi;
+  const bool bt = p.flags & GEMMEPI_FLAG_B_TRANS;
+  const bool per_col = p.flags & GEMMEPI_FLAG_BIAS_PER_COL;
+  const bool unfused = p.flags & GEMMEPI_FLAG_UNFUSED;
+  const bool needs_bias = epi != EPI_DEFAULT;  // DRELU_BGRAD: bgrad output
+  const bool needs_aux = epi == EPI_RELU_AUX_BIAS || epi == EPI_DRELU_BGRAD;
+
+  if (!A || !B || !out) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: A, B and out are required");
+  if (needs_bias && !bias)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs the bias pointer%s",
+                epi == EPI_DRELU_BGRAD ? " (fp32 bgrad output)" : "");
+  if (needs_aux && !aux) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs aux");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute: A, B and out must be 16-byte aligned");
+  if (needs_bias && !aligned(bias, epi == EPI_DRELU_BGRAD ? 4 : 2))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute: bias misaligned");
+  if (needs_aux && !aligned(aux, 16))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute: aux must be 16-byte aligned");
+
+  gemmepi_status_t st = check_device();
+  if (st != GEMMEPI_OK) return st;
+  if (p.flags & GEMMEPI_FLAG_VALIDATE) {
+    if ((st = check_device_ptr(A, "A")) != GEMMEPI_OK) return st;
+    if ((st = check_device_ptr(B, "B")) != GEMMEPI_OK) return st;
+    if ((st = check_device_ptr(out, "out")) != GEMMEPI_OK) return st;
+    if (needs_bias && (st = check_device_ptr(bias, "bias")) != GEMMEPI_OK) return st;
+    if (needs_aux && (st = check_device_ptr(aux, "aux")) != GEMMEPI_OK) return st;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const int M = (int)p.M, N = (int)p.N, K = (int)p.K;
+  const int aux_ld = (int)gemmepi_aux_ld_words(N);
+  const int core_epi = unfused ? EPI_DEFAULT : epi;
+  hipError_t e = hipSuccess;
+  (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
+
+  if (epi == EPI_DRELU_BGRAD) {
+    e = launch_fill_f32((float*)bias, N, 0.0f, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "bgrad fill: %s", hipGetErrorString(e));
+  }
+
+  if (p.path == PATH_DECODE) {
+    DecodeArgs d;
+    d.x = A;
+    d.W = B;
+    d.bias = bias;
+    d.out = out;
+    d.M = M;
+    d.N = N;
+    d.K = K;
+    d.ldx = K;
+    d.ldw = K;
+    d.ldo = N;
+    d.k_per_wave = p.k_per_wave;
+    d.epi = core_epi;
+    d.bias_per_col = per_col ? 1 : 0;
+    e = launch_decode(p.dtype, d, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "decode kernel: %s", hipGetErrorString(e));
+  } else {
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.bias = bias;
+    g.aux = (uint32_t*)aux;
+    g.out = out;
+    g.bgrad = (float*)bias;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.lda = K;
+    g.ldb = bt ? K : N;
+    g.ldo = N;
+    g.aux_ld = aux_ld;
+    g.aux_words = (N + 31) / 32;
+    g.epi = core_epi;
+    g.bias_per_col = per_col ? 1 : 0;
+    g.tiles_m = p.tiles_m;
+    g.tiles_n = p.tiles_n;
+    g.group_m = p.group_m;
+    g.xcd_remap = p.xcd_remap;
+    e = launch_gemm(p.dtype, bt, p.tile, g, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
+  }
+
+  if (unfused) {
+    switch (epi) {
+      case EPI_DEFAULT:
+        break;
+      case EPI_DRELU_BGRAD:
+        e = launch_mask_apply(p.dtype, out, (const uint32_t*)aux, M, N, N, aux_ld, s);
+        if (e == hipSuccess) e = launch_colsum(p.dtype, out, (float*)bias, M, N, N, s);
+        break;
+      default:
+        e = launch_bias_add(p.dtype, out, bias, M, N, N, per_col ? 1 : 0, s);
+        if (e == hipSuccess && epi != EPI_BIAS)
+          e = launch_activation(p.dtype, epi, out, (uint32_t*)aux, M, N, N, aux_ld, s);
+        break;
+    }
+    if (e != hipSuccess)
+      return fail(GEMMEPI_ERR_HIP, "unfused elementwise kernel: %s", hipGetErrorString(e));
+  }
+  return GEMMEPI_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// Internal interface between the C-ABI host code and the HIP kernels of
+// libgemmepi.  Not installed; callers use include/gemmepi.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gemmepi {
+
+enum Epi : int {
+  EPI_DEFAULT = 0,
+  EPI_BIAS = 1,
+  EPI_RELU_BIAS = 2,
+  EPI_RELU_AUX_BIAS = 3,
+  EPI_GELU_BIAS = 4,
+  EPI_DRELU_BGRAD = 5
+};
+
+enum DType : int { DT_F16 = 0, DT_BF16 = 1 };
+
+// Arguments of the tiled MFMA GEMM kernel (passed by value).
+struct GemmArgs {
+  const void* A;     // [M, lda] row-major
+  const void* B;     // [K, ldb] or, transposed, [N, ldb]
+  const void* bias;  // [M] or [N] in the input dtype (BIAS-type epilogues)
+  uint32_t* aux;     // packed mask [M, aux_ld] (out for RELU_AUX, in for DRELU)
+  void* out;         // [M, ldo]
+  float* bgrad;      // [N] fp32, pre-zeroed (DRELU_BGRAD)
+  int M, N, K;
+  int lda, ldb, ldo;
+  int aux_ld;        // words per mask row
+  int aux_words;     // ceil(N / 32): valid words per mask row
+  int epi;           // Epi
+  int bias_per_col;  // bias indexed by n (1) or by m (0)
+  int tiles_m, tiles_n;
+  int group_m;       // rows of tiles per raster group
+  int xcd_remap;     // 1: give each XCD a contiguous run of tiles
+};
+
+// Arguments of the thin-M decode kernel.
+struct DecodeArgs {
+  const void* x;     // [M, ldx] activations, M <= 16
+  const void* W;     // [N, ldw] weights, K contiguous
+  const void* bias;
+  void* out;         // [M, ldo]
+  int M, N, K;
+  int ldx, ldw, ldo;
+  int k_per_wave;    // K range of one wave (multiple of 32)
+  int epi;
+  int bias_per_col;
+};
+
+// One tile configuration of the tiled GEMM.
+struct TileCfg {
+  int bm, bn, bk, wm, wn;
+  const char* name;
+};
+
+constexpr int kNumTiles = 6;
+extern const TileCfg kTiles[kNumTiles];
+
+// Launchers (defined in the per-dtype/per-layout instantiation files).
+// Return hipSuccess or the launch error.
+hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s);
+hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
+
+// Unfused baseline kernels and helpers (elementwise.hip).
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+hipError_t launch_bias_add(int dtype, void* out, const void* bias, int M, int N, int ldo,
+                           int per_col, hipStream_t s);
+hipError_t launch_activation(int dtype, int epi, void* out, uint32_t* aux, int M, int N, int ldo,
+                             int aux_ld, hipStream_t s);
+hipError_t launch_mask_apply(int dtype, void* out, const uint32_t* aux, int M, int N, int ldo,
+                             int aux_ld, hipStream_t s);
+hipError_t launch_colsum(int dtype, const void* dz, float* bgrad, int M, int N, int ldo,
+                         hipStream_t s);
+
+// per-dtype launcher tables filled by each instantiation file
+using GemmLauncher = hipError_t (*)(const GemmArgs&, hipStream_t);
+hipError_t launch_gemm_f16_bn(int tile, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f16_bt(int tile, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16_bn(int tile, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16_bt(int tile, const GemmArgs& a, hipStream_t s);
+
+}  // namespace gemmepi

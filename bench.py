@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-epilogue GEMM suite on one MI355X.
+
+One step = one fused execution of every workload of the suite, in order:
+  C0  BIAS          W[1024,2048] X[2048,512] + b[1024]
+  C1  GELU_BIAS     decode x[T,4096] W[4096,4096]^T, T = 1, 4, 16
+                    (weights rotated over 16 copies, 512 MiB, so every read is
+                    cold in L2 and in the 256 MB Infinity Cache)
+  C2  FFN           x[tok,4096] -> GELU_BIAS(W1 [11008,4096]) -> BIAS(W2 [4096,11008]),
+                    tok = 512, 2048, 4x512, 16x128
+  C3  RELU_AUX_BIAS A[65536,16384] B[16384,8192] + bias[65536] + mask, fp16 and bf16
+  C4  DRELU_BGRAD   dY[8192,16384] W[16384,4096], mask, bgrad[4096]
+value = algorithmic FLOPs of one step (2MNK per GEMM) / step time, in TFLOP/s.
+
+Also printed in the same JSON line: per-workload fused and unfused time,
+TFLOP/s or GB/s, fraction of the roofline and fusion speedup; the roofline
+of the dominant kernel (the C3 fp16 GEMM, timed with HIP events on the stream
+it is launched on); and the CPU oracle timed on a bounded sample on this
+host.  Inputs are seeded synthetic data already resident in HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_GBS = 8000.0        # MI355X HBM3E
+DECODE_COPIES = 16
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--reps", type=int, default=0, help="reps per workload timing (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of workloads (c0,c1,c2,c3,c4)")
+    return ap.parse_args()
+
+
+def torch_dtype(dtype):
+    import torch
+    return torch.float16 if dtype == "f16" else torch.bfloat16
+
+
+def upload_bits(bits, dtype, device):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+    return t.view(torch_dtype(dtype))
+
+
+def upload_words(words, device):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(device)
+
+
+class Workload:
+    """Device buffers + fused and unfused plans of one GEMM call."""
+
+    def __init__(self, name, case, flags=0, A_dev=None, B_dev=None, out=None):
+        import torch
+        import activation_epilogue_gemm_amd as ge
+        self.name = name
+        self.case = case
+        c = case
+        dev = "cuda"
+        tdt = torch_dtype(c.dtype)
+        self.A = A_dev if A_dev is not None else (
+            c.A_dev if getattr(c, "A_dev", None) is not None else upload_bits(c.A, c.dtype, dev))
+        self.B = B_dev if B_dev is not None else (
+            c.B_dev if getattr(c, "B_dev", None) is not None else upload_bits(c.B, c.dtype, dev))
+        self.out = out if out is not None else torch.empty(c.M, c.N, dtype=tdt, device=dev)
+        self.bias = self.aux = None
+        if c.epilogue == "DRELU_BGRAD":
+            self.bias = torch.empty(c.N, dtype=torch.float32, device=dev)
+            self.aux = upload_words(c.aux, dev)
+        else:
+            if c.bias is not None:
+                self.bias = upload_bits(c.bias, c.dtype, dev)
+            if c.epilogue == "RELU_AUX_BIAS":
+                self.aux = torch.empty(c.M, ge.aux_ld_words(c.N), dtype=torch.int32, device=dev)
+        f = flags | (ge.FLAG_B_TRANS if c.b_trans else 0) | (ge.FLAG_BIAS_PER_COL if c.bias_per_col else 0)
+        self.fused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f)
+        self.unfused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f | ge.FLAG_UNFUSED)
+        self.flops = 2.0 * c.M * c.N * c.K
+        # algorithmic bytes: each operand, bias, output, aux and bgrad moved once
+        esz = 2
+        self.bytes = esz * (c.M * c.K + c.N * c.K + c.M * c.N)
+        if self.bias is not None:
+            self.bytes += self.bias.numel() * self.bias.element_size()
+        if self.aux is not None:
+            self.bytes += self.aux.numel() * 4
+        self.rotation = None  # list of (A, B, out) for cache-cold decode timing
+
+    def run(self, unfused=False, i=0):
+        p = self.unfused if unfused else self.fused
+        if self.rotation:
+            A, B, out = self.rotation[i % len(self.rotation)]
+        else:
+            A, B, out = self.A, self.B, self.out
+        p.execute(A, B, self.bias, self.aux, out, check=False)
+
+
+def build_suite(only):
+    import torch
+    import workloads as wl
+    sel = set(only.split(",")) if only else {"c0", "c1", "c2", "c3", "c4"}
+    suite = []
+    t0 = time.time()
+    if "c0" in sel:
+        suite.append(Workload("c0_bias", wl.config0_bias()))
+    if "c1" in sel:
+        for T in (1, 4, 16):
+            w = Workload(f"c1_decode_T{T}", wl.config1_decode(T))
+            w.rotation = [(w.A, w.B.clone(), torch.empty_like(w.out)) for _ in range(DECODE_COPIES)]
+            suite.append(w)
+    if "c2" in sel:
+        W1 = W2 = None  # one copy of the FFN weights shared by all token variants
+        for v in wl.FFN_TOKENS:
+            up, down = wl.config2_ffn(v)
+            wu = Workload(f"c2_{v}_up", up, B_dev=W1)
+            wd = Workload(f"c2_{v}_down", down, A_dev=wu.out, B_dev=W2)
+            W1, W2 = wu.B, wd.B
+            suite += [wu, wd]
+    if "c3" in sel:
+        for dt in ("f16", "bf16"):
+            suite.append(Workload(f"c3_relu_aux_{dt}", wl.config3_relu_aux(dt)))
+    if "c4" in sel:
+        suite.append(Workload("c4_drelu_bgrad", wl.config4_drelu_bgrad()))
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s; device memory "
+        f"{torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+    return suite
+
+
+def time_region(fn, reps, stream):
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(reps):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps  # ms
+
+
+def bench_workload(w, reps, stream):
+    """Median of 3 trials of `reps` back-to-back executions, fused and unfused."""
+    import statistics
+    res = {}
+    for label, unf in (("fused", False), ("unfused", True)):
+        for i in range(2):
+            w.run(unf, i)
+        trials = [time_region(lambda i: w.run(unf, i), reps, stream) for _ in range(3)]
+        res[label] = statistics.median(trials)
+    return res
+
+
+def cpu_baseline(seconds_target=15.0):
+    """The oracle, as it stands, on a bounded sample of the C3 workload
+    (fp16): a few hundred sampled output rows against the full B."""
+    import numpy as np
+    import torch
+    import workloads as wl
+    from oracle import oracle as O
+    cores = len(os.sched_getaffinity(0))
+    c = wl.config3_relu_aux("f16")
+    B = c.host_B()
+    rows_all = wl.sample_rows(c.M, 4096, wl.row_sample_seed(3))
+    # calibrate on 64 rows, then size the timed sample to ~seconds_target
+    probe = rows_all[:64]
+    t = time.perf_counter()
+    O.gemm_epilogue(c.host_A(probe), B, c.bias[probe], None, len(probe), c.N, c.K, "f16",
+                    "RELU_AUX_BIAS", False, False)
+    dt = time.perf_counter() - t
+    nrows = int(max(64, min(4096, 64 * seconds_target / max(dt, 1e-3))))
+    rows = rows_all[:nrows]
+    A_rows = c.host_A(rows)
+    t = time.perf_counter()
+    O.gemm_epilogue(A_rows, B, c.bias[rows], None, len(rows), c.N, c.K, "f16", "RELU_AUX_BIAS",
+                    False, False)
+    dt = time.perf_counter() - t
+    del c
+    torch.cuda.empty_cache()
+    flops = 2.0 * len(rows) * 8192 * 16384
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=cores)
+    except Exception:
+        threads = cores
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"C3 fp16 RELU_AUX_BIAS, {len(rows)} sampled rows of 65536 "
+                      f"(x 8192 cols, K=16384; fp64 numpy), {dt:.1f} s, host cores {cores}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by output tiles; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import activation_epilogue_gemm_amd as ge
+    ge.library()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "no GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    props = torch.cuda.get_device_properties(0)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs {props.multi_processor_count}")
+
+    suite = build_suite(args.only)
+    for w in suite:
+        log(f"{w.name}: {w.fused.info()}")
+
+    def step(i):
+        for w in suite:
+            w.run(False, i)
+
+    # warmup + timed steps (the whole suite, fused)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+    step_flops = sum(w.flops for w in suite)
+    log(f"step {ms_step:.3f} ms (wall {1e3 * wall / args.steps:.3f} ms), "
+        f"{step_flops / ms_step / 1e9:.1f} TFLOP/s")
+
+    # per-workload fused / unfused timing
+    per = {}
+    for w in suite:
+        reps = args.reps
+        if not reps:
+            t = time_region(lambda i: w.run(False, i), 3, stream)
+            reps = int(max(5, min(200, 150.0 / max(t, 1e-3))))
+        r = bench_workload(w, reps, stream)
+        f_ms, u_ms = r["fused"], r["unfused"]
+        entry = {"fused_ms": round(f_ms, 5), "unfused_ms": round(u_ms, 5),
+                 "speedup": round(u_ms / f_ms, 4), "reps": reps,
+                 "tflops": round(w.flops / f_ms / 1e9, 2),
+                 "frac_mfma_peak": round(w.flops / f_ms / 1e9 / PEAK_TFLOPS, 4),
+                 "plan": w.fused.info()}
+        if w.name.startswith("c1_"):
+            gbs = w.bytes / f_ms / 1e6
+            entry.update({"gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_GBS, 4),
+                          "bytes": w.bytes})
+        per[w.name] = entry
+        log(f"{w.name}: fused {f_ms:.4f} ms unfused {u_ms:.4f} ms "
+            f"x{u_ms / f_ms:.3f} {entry['tflops']} TFLOP/s" +
+            (f" {entry['gbs']} GB/s" if "gbs" in entry else ""))
+
+    # roofline of the dominant kernel: the C3 fp16 fused GEMM
+    dom = next((w for w in suite if w.name == "c3_relu_aux_f16"), None) or \
+        max(suite, key=lambda w: w.flops)
+    reps = 20 if dom.flops > 1e12 else 200
+    ms = time_region(lambda i: dom.run(False, i), reps, stream)
+    achieved = dom.flops / ms / 1e9
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": dom.name, "avg_launch_ms": round(ms, 5)}
+    log(f"roofline {dom.name}: {achieved:.1f} TFLOP/s = {achieved / PEAK_TFLOPS:.3f} of peak")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {cpu}")
+
+    names = [w.name for w in suite]
+    rec = {
+        "metric": "fused GEMM+bias/act TFLOP/s (% MFMA peak); decode-shape GB/s (% HBM)",
+        "value": round(step_flops / ms_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16+bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": "fused-epilogue GEMM suite: " + ", ".join(names),
+                   "step_tflop": round(step_flops / 1e12, 4),
+                   "frac_mfma_peak": round(step_flops / ms_step / 1e9 / PEAK_TFLOPS, 4),
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "workloads": per,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

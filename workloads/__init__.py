@@ -49,13 +49,18 @@ def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even fp32 -> bf16 (upper 16 bits), as uint16 bits.
 
-    NaN never occurs in generated inputs; finite values round with ties to
-    even on the low 16 bits.
+    Finite inputs only (generated inputs never hold NaN): adding 0x7FFF plus
+    the lowest kept bit to the fp32 word and truncating rounds the low 16 bits
+    to nearest, ties to even.  Works in chunks with uint32 arithmetic.
     """
-    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    u = u + np.uint64(0x7FFF) + lsb
-    return (u >> np.uint64(16)).astype(np.uint16)
+    x = np.asarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for s in range(0, flat.size, _CHUNK):
+        u = flat[s:s + _CHUNK].view(np.uint32)
+        lsb = (u >> np.uint32(16)) & np.uint32(1)
+        out[s:s + _CHUNK] = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    return out.reshape(x.shape)
 
 
 def to_bits(x32: np.ndarray, dtype: str) -> np.ndarray:
@@ -222,20 +227,61 @@ def config2_ffn(variant: str, dtype: str = F16):
     return up, down
 
 
-def config3_relu_aux(dtype: str = F16, M: int = 65536, N: int = 8192, K: int = 16384) -> GemmCase:
-    """out = relu(A[M,K] B[K,N] + bias[M]) plus the packed ReLU mask."""
-    c = GemmCase(f"c3_relu_aux_{dtype}", M, N, K, dtype, "RELU_AUX_BIAS", False, False)
-    c.A = normal((M, K), seed_of(3, 0), 1.0 / 128.0, dtype)
-    c.B = normal((K, N), seed_of(3, 1), 1.0, dtype)
+def device_normal(shape, seed: int, std: float, dtype: str, device="cuda"):
+    """N(0, std^2) drawn on the GPU with torch's seeded Philox generator in
+    fp32, scaled, then rounded to the storage dtype (round to nearest even).
+    Used for the two large workloads, whose operands (up to 2^30 elements)
+    would take minutes to draw on the host.  The oracle reads the exact same
+    bits back from device memory (these are inputs; no kernel of the library
+    touches them before that)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(float(std))
+    y = x.to(torch.float16 if dtype == F16 else torch.bfloat16)
+    del x
+    return y
+
+
+@dataclasses.dataclass
+class DeviceCase(GemmCase):
+    """A GemmCase whose A and B live in device memory (torch tensors);
+    ``host_A(rows)`` / ``host_B()`` return their storage bits for the oracle."""
+    A_dev: object = None
+    B_dev: object = None
+
+    def host_A(self, rows=None) -> np.ndarray:
+        import torch
+        a = self.A_dev
+        if rows is not None:
+            a = a.index_select(0, torch.as_tensor(np.asarray(rows), device=a.device))
+        return a.view(torch.int16).cpu().numpy().view(np.uint16)
+
+    def host_B(self) -> np.ndarray:
+        import torch
+        return self.B_dev.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def config3_relu_aux(dtype: str = F16, device="cuda", M: int = 65536, N: int = 8192,
+                     K: int = 16384) -> DeviceCase:
+    """out = relu(A[M,K] B[K,N] + bias[M]) plus the packed ReLU mask.
+    A ~ N(0,1)/128, B ~ N(0,1), bias ~ N(0,1) (per row)."""
+    c = DeviceCase(f"c3_relu_aux_{dtype}", M, N, K, dtype, "RELU_AUX_BIAS", False, False)
+    c.A_dev = device_normal((M, K), seed_of(3, 0), 1.0 / 128.0, dtype, device)
+    c.B_dev = device_normal((K, N), seed_of(3, 1), 1.0, dtype, device)
     c.bias = normal((M,), seed_of(3, 2), 1.0, dtype)
     return c
 
 
-def config4_drelu_bgrad(dtype: str = F16, M: int = 8192, N: int = 4096, K: int = 16384) -> GemmCase:
-    """dZ = mask ? dY[M,K] W[K,N] : 0 and bgrad[N] = column sums of dZ."""
-    c = GemmCase(f"c4_drelu_bgrad_{dtype}", M, N, K, dtype, "DRELU_BGRAD", False, False)
-    c.A = normal((M, K), seed_of(4, 0), 1.0 / 128.0, dtype)
-    c.B = normal((K, N), seed_of(4, 1), 1.0 / 128.0, dtype)
+def config4_drelu_bgrad(dtype: str = F16, device="cuda", M: int = 8192, N: int = 4096,
+                        K: int = 16384) -> DeviceCase:
+    """dZ = mask ? dY[M,K] W[K,N] : 0 and bgrad[N] = column sums of dZ;
+    dY, W ~ N(0,1)/128, mask bits Bernoulli(0.5)."""
+    c = DeviceCase(f"c4_drelu_bgrad_{dtype}", M, N, K, dtype, "DRELU_BGRAD", False, False)
+    c.A_dev = device_normal((M, K), seed_of(4, 0), 1.0 / 128.0, dtype, device)
+    c.B_dev = device_normal((K, N), seed_of(4, 1), 1.0 / 128.0, dtype, device)
     c.aux = random_mask(M, N, seed_of(4, 2))
     return c
 

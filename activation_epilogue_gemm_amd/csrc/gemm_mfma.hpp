@@ -17,12 +17,11 @@
 //     (BM/WM) x (BN/WN) sub-tile made of 32x32 MFMA tiles;
 //   * K is walked in slabs of BK.  Each slab of A [BM x BK] and of B is
 //     fetched with 128-bit buffer loads that write straight into LDS (no
-//     register staging), into one of two stage buffers, while the MFMAs
-//     consume the other stage; one barrier per slab.  Out-of-range rows,
-//     columns and k read as zero through the buffer descriptor's range
-//     check.  The two stages are separate LDS objects and the slab loop is
-//     unrolled by two, so the compiler can see that the loads in flight
-//     never alias the stage being read and does not wait for them;
+//     register staging) into a ring of NS stage buffers: while the MFMAs
+//     consume slab kt, the loads of slabs kt+1 .. kt+NS-1 are in flight, so
+//     the prefetch distance covers HBM latency even with one workgroup per
+//     CU.  One barrier per slab.  Out-of-range rows, columns and k read as
+//     zero through the buffer descriptor's range check;
 //   * LDS rows are XOR-swizzled in 16-byte units so that the 128-bit
 //     fragment reads (and the 64-bit transposing reads of a row-major [K,N]
 //     B) hit distinct banks of the 64-bank LDS;
@@ -38,6 +37,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_tiles.h"
 #include "kernels.h"
 
 namespace gemmepi {
@@ -83,9 +83,14 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint
                : "memory");
 }
 
-// Wait until every vector memory operation of this wave (including the LDS
-// writes of buffer->LDS loads) has completed.
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector memory operations of this wave are still in
+// flight (loads complete in issue order, so every older buffer->LDS load,
+// LDS write included, has then landed).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const GEMMEPI_LDS void*)p;
@@ -173,7 +178,7 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn)
   tn = r / gsz;
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int WM, int WN, int NS>
 struct GemmTile {
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
@@ -194,7 +199,9 @@ struct GemmTile {
   static_assert(BK % 16 == 0 && BK >= 32, "BK");
   static_assert(A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "load split");
   static_assert(64 % KCH == 0 && 64 % NCH == 0 && BN * 2 <= 1024, "load split");
-  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+  static constexpr int LPS = A_CH + B_CH;            // load instructions per slab per wave
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
+  static_assert((NS - 2) * LPS < 64, "vmcnt range");
   static_assert(WM * BN * 4 <= STAGE, "bias-gradient scratch");
 
   // 16 B-chunk swizzle of a K-contiguous row r (A, or B stored [N,K])
@@ -203,15 +210,14 @@ struct GemmTile {
   static __device__ __forceinline__ int swz_n(int kr) { return (4 * (kr / RPN)) % NCH; }
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool BT>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT>
 __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p) {
-  using G = GemmTile<BM, BN, BK, WM, WN>;
+  using G = GemmTile<BM, BN, BK, WM, WN, NS>;
   using V8 = typename Frag<T>::type;
   constexpr int NT = G::NT, NW = G::NW, WTM = G::WTM, WTN = G::WTN, FM = G::FM, FN = G::FN;
   constexpr int KCH = G::KCH, NCH = G::NCH, A_CH = G::A_CH, B_CH = G::B_CH;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t stage0[G::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t stage1[G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -329,21 +335,31 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     }
   };
 
-  issue(0, stage0);
-  wait_loads();
+  // prologue: slabs 0 .. NS-2 in flight, wait for slab 0
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < KT) issue(s, smem + s * G::STAGE);
+  if (KT >= NS - 1)
+    wait_vmcnt<(NS - 2) * G::LPS>();
+  else
+    wait_vmcnt<0>();
   __syncthreads();
-  int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {  // two slabs per trip: stage0 then stage1
-    issue(kt + 1, stage1);
-    compute(stage0);
-    wait_loads();
+  int cur = 0;                      // stage of slab kt
+  int nxt = NS - 1;                 // stage that receives slab kt + NS - 1
+  for (int kt = 0; kt < KT; ++kt) {
+    // the stage of slab kt-1 is free: every wave passed the last barrier
+    const bool more = kt + NS - 1 < KT;
+    if (more) issue(kt + NS - 1, smem + nxt * G::STAGE);
+    compute(smem + cur * G::STAGE);
+    // slab kt+1 must have landed; slabs kt+2 .. kt+NS-1 may stay in flight
+    if (more)
+      wait_vmcnt<(NS - 2) * G::LPS>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 2 < KT) issue(kt + 2, stage0);
-    compute(stage1);
-    wait_loads();
-    __syncthreads();
+    cur = (cur + 1 == NS) ? 0 : cur + 1;
+    nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
   }
-  if (kt < KT) compute(stage0);  // odd slab count: the last slab is in stage0
 
   // ---- epilogue on the accumulators -----------------------------------------
   // lane owns row m = wrow0 + 32 fm + lrow and, in tile (fm, fn), columns
@@ -410,7 +426,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         v += __shfl_xor(v, 16);
         cs[fn][r] = v;
       }
-    float* red = (float*)stage0;  // [WM][BN] column sums per wave row
+    float* red = (float*)smem;  // [WM][BN] column sums per wave row
     if (lrow == 0) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
@@ -473,25 +489,24 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   }
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool BT>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
   const int blocks = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, BT>), dim3(blocks), dim3(WM * WN * 64), 0,
-                     s, a);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, NS, BT>), dim3(blocks), dim3(WM * WN * 64),
+                     0, s, a);
   return hipGetLastError();
 }
 
-// The tile table: must match kTiles in gemmepi_api.cpp.
 template <typename T, bool BT>
 hipError_t launch_by_tile(int tile, const GemmArgs& a, hipStream_t s) {
   switch (tile) {
-    case 0: return launch_tile<T, 256, 256, 64, 2, 2, BT>(a, s);
-    case 1: return launch_tile<T, 256, 256, 64, 2, 4, BT>(a, s);
-    case 2: return launch_tile<T, 256, 128, 64, 2, 2, BT>(a, s);
-    case 3: return launch_tile<T, 128, 128, 64, 2, 2, BT>(a, s);
-    case 4: return launch_tile<T, 128, 64, 64, 2, 2, BT>(a, s);
-    case 5: return launch_tile<T, 64, 64, 64, 2, 2, BT>(a, s);
-    default: return hipErrorInvalidValue;
+#define GEMMEPI_CASE(id, bm, bn, bk, wm, wn, ns) \
+  case id:                                       \
+    return launch_tile<T, bm, bn, bk, wm, wn, ns, BT>(a, s);
+    GEMMEPI_TILES(GEMMEPI_CASE)
+#undef GEMMEPI_CASE
+    default:
+      return hipErrorInvalidValue;
   }
 }
 

@@ -22,21 +22,24 @@
 #include <tuple>
 
 #include "gemmepi.h"
+#include "gemm_tiles.h"
 #include "kernels.h"
 
 namespace gemmepi {
 
-const TileCfg kTiles[kNumTiles] = {
-    {256, 256, 64, 2, 2, "256x256x64_w2x2"}, {256, 256, 64, 2, 4, "256x256x64_w2x4"},
-    {256, 128, 64, 2, 2, "256x128x64_w2x2"}, {128, 128, 64, 2, 2, "128x128x64_w2x2"},
-    {128, 64, 64, 2, 2, "128x64x64_w2x2"},   {64, 64, 64, 2, 2, "64x64x64_w2x2"},
-};
+#define GEMMEPI_TILE_ENTRY(id, bm, bn, bk, wm, wn, ns) \
+  {bm, bn, bk, wm, wn, ns, #bm "x" #bn "x" #bk "_w" #wm "x" #wn "_s" #ns},
+const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
+#undef GEMMEPI_TILE_ENTRY
 
 // Relative throughput of one CU on a full tile of each configuration, and
 // how many of its workgroups fit on one CU (LDS and registers).  Used only
-// to rank tiles for a shape: est = rounds * occupancy * BM * BN / eff.
-static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.55, 0.40};
-static const int kTileOcc[kNumTiles] = {1, 1, 1, 2, 3, 4};
+// to rank tiles for a shape: the grid runs in `rounds` of up to
+// kNumCU * occ tiles; in one round a CU holds up to `occ` tiles that share
+// its MFMA units, so
+//   est = rounds * min(occ, ceil(tiles / kNumCU)) * BM * BN / eff.
+static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.86, 0.82, 0.70, 0.66, 0.56};
+static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 1, 2, 3};
 constexpr int kNumCU = 256;
 
 hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s) {
@@ -107,7 +110,9 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
     const int64_t slots = (int64_t)kNumCU * kTileOcc[t];
     const int64_t rounds = (tiles + slots - 1) / slots;
-    const double est = (double)rounds * kTileOcc[t] * c.bm * c.bn / kTileEff[t];
+    const int64_t per_cu = (tiles + kNumCU - 1) / kNumCU;
+    const int64_t share = per_cu < kTileOcc[t] ? per_cu : kTileOcc[t];
+    const double est = (double)rounds * share * c.bm * c.bn / kTileEff[t];
     if (t == 0 || est < best_est) {
       best = t;
       best_est = est;

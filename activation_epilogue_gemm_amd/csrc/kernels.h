@@ -53,11 +53,11 @@ struct DecodeArgs {
 
 // One tile configuration of the tiled GEMM.
 struct TileCfg {
-  int bm, bn, bk, wm, wn;
+  int bm, bn, bk, wm, wn, ns;
   const char* name;
 };
 
-constexpr int kNumTiles = 6;
+constexpr int kNumTiles = 7;
 extern const TileCfg kTiles[kNumTiles];
 
 // Launchers (defined in the per-dtype/per-layout instantiation files).

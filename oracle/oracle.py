@@ -24,8 +24,8 @@ with these epilogues (the MatmulEpilog members the pages name):
                  paragraph 1)
   RELU_AUX_BIAS  as RELU_BIAS plus the ReLU mask (z > 0) kept as an auxiliary
                  output ("Fusing bias addition ...", paragraph 4)
-  GELU_BIAS      y = 0.5 z (1 + erf(z / sqrt 2)), the exact (erf) GELU that the
-                 unfused code of the ops-nn article calls by default
+  GELU_BIAS      y = z Phi(z) = 0.5 z erfc(-z / sqrt 2), the exact (erf) GELU
+                 that the unfused code of the ops-nn article calls by default
   DRELU_BGRAD    backward of ReLU+bias: dZ = mask ? acc : 0 and
                  bgrad[j] = sum_i dZ[i,j] ("nvmath-python cuBLASLt bias fusion
                  guide", section "Advanced techniques and engineering practice")
@@ -131,13 +131,16 @@ def encode(y: np.ndarray, dtype: str) -> np.ndarray:
 # --------------------------------------------------------------------------
 # epilogue pieces
 # --------------------------------------------------------------------------
-_erf = np.frompyfunc(math.erf, 1, 1)
+_erfc = np.frompyfunc(math.erfc, 1, 1)
 
 
 def gelu(z: np.ndarray) -> np.ndarray:
-    """Exact GELU, z * Phi(z) = 0.5 z (1 + erf(z / sqrt 2)), with libm erf."""
+    """Exact GELU, z * Phi(z), with the standard normal CDF written through
+    libm's complementary error function, Phi(z) = erfc(-z / sqrt 2) / 2.
+    This equals 0.5 z (1 + erf(z / sqrt 2)) but does not cancel to zero in
+    the negative tail (1 + erf(x) rounds to 0 in fp64 below x ~ -5.9)."""
     z = np.asarray(z, dtype=np.float64)
-    return 0.5 * z * (1.0 + _erf(z / math.sqrt(2.0)).astype(np.float64))
+    return 0.5 * z * _erfc(-z / math.sqrt(2.0)).astype(np.float64)
 
 
 def aux_ld_words(n: int) -> int:

@@ -102,7 +102,7 @@ def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
                 y = z if z > 0 else 0.0
                 mrow.append(z > 0)
             elif epilogue == "GELU_BIAS":
-                y = 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0)))
+                y = 0.5 * z * math.erfc(-z / math.sqrt(2.0))
             elif epilogue == "DRELU_BGRAD":
                 bit = (mask_words[i][j >> 5] >> (j & 31)) & 1
                 y = z if bit else 0.0

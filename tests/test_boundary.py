@@ -53,7 +53,7 @@ def test_plan_validation():
     assert _plan_status(64, 64, 64, epi=6) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, epi=-1) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, flags=1 << 9) == ge.ERR_INVALID_VALUE
-    assert _plan_status(64, 64, 64, tile=6) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, tile=ge.num_tiles()) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 60) == ge.ERR_MISALIGNED          # K % 8
     assert _plan_status(64, 60, 64) == ge.ERR_MISALIGNED          # N % 8 without B_TRANS
     assert _plan_status(64, 60, 64, flags=ge.FLAG_B_TRANS) == ge.OK
@@ -92,7 +92,7 @@ def test_plan_paths_and_tiles():
     with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", 0) as p:   # B not transposed: no decode
         assert "path=gemm" in p.info()
     with ge.plan(65536, 8192, 16384, "f16", "RELU_AUX_BIAS", 0) as p:
-        assert "tile=256x256x64" in p.info() and "xcd_remap=1" in p.info()
+        assert "tile=256x256" in p.info() and "xcd_remap=1" in p.info()
     for t in range(ge.num_tiles()):
         name = ge.tile_name(t)
         assert re.match(r"\d+x\d+x\d+_w\dx\d", name)

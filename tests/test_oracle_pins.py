@@ -139,6 +139,15 @@ def test_gelu_against_normal_table():
             assert abs(got - want) <= 1e-15 * max(1.0, abs(want)), (zz, got, want)
 
 
+def test_gelu_negative_tail():
+    """gelu(-z) = -z Q(z) keeps its relative accuracy far into the tail
+    (bf16 outputs can represent values down to ~1e-40)."""
+    g = _golden("normal_cdf.json")
+    for z, q in g["tail"]:
+        got = float(O.gelu(np.array([-z]))[0])
+        assert abs(got - (-z * q)) <= 1e-11 * abs(z * q), (z, got, -z * q)
+
+
 def test_gelu_identities():
     z = np.linspace(-12, 12, 2001)
     g = O.gelu(z)

@@ -160,14 +160,32 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * one_plus_erf;
 }
 
-// blockIdx -> output tile.  With xcd_remap, the hardware's round-robin of
-// consecutive workgroups over the 8 XCDs is undone so that each XCD (with
-// its own L2) walks a contiguous run of the tile order; the tile order is
-// grouped by `group_m` tile rows so that concurrently running tiles share
-// A row panels and B column panels.
+// blockIdx -> output tile.  The hardware hands consecutive workgroup ids
+// to the 8 XCDs round-robin (id % 8), and each XCD has its own L2.
+//  * Chip-block raster (sb_m > 0): the tiles run in rounds of sb_m x sb_n
+//    (one per CU), rounds ordered along N; inside a round XCD x takes a
+//    (sb_m / xcd_m) x (sb_n / xcd_n) sub-block.  Concurrent tiles of one XCD
+//    share their A and B panels in its L2, and the whole chip's concurrent
+//    tiles touch only sb_m + sb_n panels, which the XCDs share through the
+//    Infinity Cache instead of each reading them from HBM.
+//  * Otherwise (shapes that do not divide): with xcd_remap each XCD walks a
+//    contiguous run of the tile order, grouped by `group_m` tile rows.
 __device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
   int bid = blockIdx.x;
   const int nb = gridDim.x;
+  if (p.sb_m > 0) {
+    const int x = bid & 7;                 // XCD of this workgroup
+    const int j = bid >> 3;                // its index on that XCD
+    const int per_xcd = (p.sb_m * p.sb_n) >> 3;
+    const int round = j / per_xcd, slot = j - round * per_xcd;
+    const int sub_n = p.sb_n / p.xcd_n;
+    const int rounds_n = p.tiles_n / p.sb_n;
+    const int rm = round / rounds_n, rn = round - rm * rounds_n;
+    const int xm = x / p.xcd_n, xn = x - xm * p.xcd_n;
+    tm = rm * p.sb_m + xm * (p.sb_m / p.xcd_m) + slot / sub_n;
+    tn = rn * p.sb_n + xn * sub_n + slot % sub_n;
+    return;
+  }
   if (p.xcd_remap) bid = (bid & 7) * (nb >> 3) + (bid >> 3);
   const int per_group = p.group_m * p.tiles_n;
   const int g = bid / per_group;

@@ -62,6 +62,7 @@ struct gemmepi_plan_s {
   int path;
   int tile;
   int tiles_m, tiles_n, group_m, xcd_remap;
+  int sb_m, sb_n, xcd_m, xcd_n;
   int k_per_wave;
   int refs;
   std::string info;
@@ -136,9 +137,10 @@ void describe(gemmepi_plan_s* p) {
     const TileCfg& c = kTiles[p->tile];
     snprintf(buf, sizeof(buf),
              "path=gemm M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x tile=%s tiles=%dx%d "
-             "group_m=%d xcd_remap=%d%s",
+             "raster=%s%s",
              (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
-             epis[p->epi], p->flags, c.name, p->tiles_m, p->tiles_n, p->group_m, p->xcd_remap,
+             epis[p->epi], p->flags, c.name, p->tiles_m, p->tiles_n,
+             p->sb_m ? "chip16x16/xcd4x8" : (p->xcd_remap ? "xcd_remap,group8" : "group8"),
              (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
   }
   p->info = buf;
@@ -247,6 +249,17 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
     p->group_m = p->tiles_m < 8 ? p->tiles_m : 8;
     const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
     p->xcd_remap = (tiles % 8 == 0 && tiles >= 64) ? 1 : 0;
+    // chip-block raster when one round of 16 x 16 tiles (one per CU) divides
+    // the grid; XCDs take 4 x 8 sub-blocks (4 A panels, 8 B panels each)
+    p->sb_m = p->sb_n = p->xcd_m = p->xcd_n = 0;
+    const char* rast = getenv("GEMMEPI_RASTER");
+    const bool chip_ok = kTileOcc[p->tile] == 1 && p->tiles_m % 16 == 0 && p->tiles_n % 16 == 0;
+    if (chip_ok && !(rast && rast[0] == '0')) {
+      p->sb_m = 16;
+      p->sb_n = 16;
+      p->xcd_m = 4;
+      p->xcd_n = 2;
+    }
   }
   describe(p);
   if (log_enabled()) fprintf(stderr, "[gemmepi] plan %s\n", p->info.c_str());
@@ -419,6 +432,10 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
     g.tiles_n = p.tiles_n;
     g.group_m = p.group_m;
     g.xcd_remap = p.xcd_remap;
+    g.sb_m = p.sb_m;
+    g.sb_n = p.sb_n;
+    g.xcd_m = p.xcd_m;
+    g.xcd_n = p.xcd_n;
     e = launch_gemm(p.dtype, bt, p.tile, g, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
   }

@@ -36,6 +36,10 @@ struct GemmArgs {
   int tiles_m, tiles_n;
   int group_m;       // rows of tiles per raster group
   int xcd_remap;     // 1: give each XCD a contiguous run of tiles
+  // chip-block raster (used when sb_m > 0): the grid runs in rounds of
+  // sb_m x sb_n tiles, one tile per CU; XCD x owns the sub-block
+  // (x / xcd_n, x % xcd_n) of (sb_m / xcd_m) x (sb_n / xcd_n) tiles.
+  int sb_m, sb_n, xcd_m, xcd_n;
 };
 
 // Arguments of the thin-M decode kernel.

@@ -92,7 +92,7 @@ def test_plan_paths_and_tiles():
     with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", 0) as p:   # B not transposed: no decode
         assert "path=gemm" in p.info()
     with ge.plan(65536, 8192, 16384, "f16", "RELU_AUX_BIAS", 0) as p:
-        assert "tile=256x256" in p.info() and "xcd_remap=1" in p.info()
+        assert "tile=256x256" in p.info() and "raster=chip16x16" in p.info()
     for t in range(ge.num_tiles()):
         name = ge.tile_name(t)
         assert re.match(r"\d+x\d+x\d+_w\dx\d", name)

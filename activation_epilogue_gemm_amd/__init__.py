@@ -95,6 +95,8 @@ def _load():
     lib.gemmepi_last_error.restype = ctypes.c_char_p
     lib.gemmepi_version.argtypes = []
     lib.gemmepi_version.restype = i32
+    lib.gemmepi_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
+    lib.gemmepi_stream_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -131,6 +133,13 @@ def aux_ld_words(N: int) -> int:
 
 def aux_bytes(M: int, N: int) -> int:
     return int(_load().gemmepi_aux_bytes(int(M), int(N)))
+
+
+def stream_read(p, nbytes: int, sink, stream=None) -> None:
+    """gemmepi_stream_read: the reference 128-bit streaming read of `nbytes`
+    bytes at `p` (measurement helper)."""
+    st = _load().gemmepi_stream_read(_ptr(p), int(nbytes), _ptr(sink), _stream_handle(stream, p, sink))
+    _check(st, "gemmepi_stream_read")
 
 
 def _check(status: int, where: str):

@@ -77,6 +77,7 @@ hipError_t launch_activation(int dtype, int epi, void* out, uint32_t* aux, int M
                              int aux_ld, hipStream_t s);
 hipError_t launch_mask_apply(int dtype, void* out, const uint32_t* aux, int M, int N, int ldo,
                              int aux_ld, hipStream_t s);
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_colsum(int dtype, const void* dz, float* bgrad, int M, int N, int ldo,
                          hipStream_t s);
 

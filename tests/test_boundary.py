@@ -24,7 +24,7 @@ def test_header_declares_the_api():
     for n in ("gemmepi_plan", "gemmepi_plan_tiled", "gemmepi_execute", "gemmepi_plan_destroy",
               "gemmepi_plan_info", "gemmepi_aux_ld_words", "gemmepi_aux_bytes",
               "gemmepi_status_string", "gemmepi_last_error", "gemmepi_num_tiles",
-              "gemmepi_tile_name", "gemmepi_version"):
+              "gemmepi_tile_name", "gemmepi_version", "gemmepi_stream_read"):
         assert n in names
 
 
@@ -136,6 +136,9 @@ def test_execute_rejects_bad_pointers_before_any_hip_call():
         # bgrad must be 4-byte aligned
         assert lib.gemmepi_execute(p._h, 4096, 4096, 4098, 4096, 4096, None) == ge.ERR_MISALIGNED
     assert lib.gemmepi_execute(None, 4096, 4096, 4096, 4096, 4096, None) == ge.ERR_INVALID_VALUE
+    assert lib.gemmepi_stream_read(None, 4096, 4096, None) == ge.ERR_INVALID_VALUE
+    assert lib.gemmepi_stream_read(4096, 0, 4096, None) == ge.ERR_INVALID_VALUE
+    assert lib.gemmepi_stream_read(4100, 4096, 4096, None) == ge.ERR_MISALIGNED
 
 
 def test_binding_checks_tensor_arguments():

@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include "gemm_tiles.h"
+
 #include "kernels.h"
 
 namespace gemmepi {
@@ -219,23 +220,39 @@ struct GemmTile {
   static_assert(64 % KCH == 0 && 64 % NCH == 0 && BN * 2 <= 1024, "load split");
   static constexpr int LPS = A_CH + B_CH;            // load instructions per slab per wave
   static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
-  static_assert((NS - 2) * LPS < 64, "vmcnt range");
-  static_assert(WM * BN * 4 <= STAGE, "bias-gradient scratch");
+  static_assert((NS - 1) * LPS < 64, "vmcnt range");
+  // epilogue: the output tile [BM][BN] and the per-wave-row column sums of
+  // the bias gradient, [WM][BN] fp32, reuse the staging ring
+  static constexpr int OUT_BYTES = BM * BN * 2;
+  static constexpr int EPI_BYTES = OUT_BYTES + WM * BN * 4;
+  static constexpr int SMEM = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert(NT % (BN / 8) == 0 && BM % (NT / (BN / 8)) == 0, "epilogue copy split");
 
   // 16 B-chunk swizzle of a K-contiguous row r (A, or B stored [N,K])
   static __device__ __forceinline__ int swz_k(int r) { return (r / RPK) % KCH; }
+  // 16 B-chunk swizzle of row r of the staged output tile
+  static __device__ __forceinline__ int swz_o(int r) { return r % (BN / 8); }
   // 16 B-chunk swizzle of an N-contiguous row kr (B stored [K,N])
   static __device__ __forceinline__ int swz_n(int kr) { return (4 * (kr / RPN)) % NCH; }
 };
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT>
+// A workgroup barrier that the instruction scheduler may not move any
+// instruction across (the ping-pong phases must stay separated).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT, int SCHED>
 __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p) {
   using G = GemmTile<BM, BN, BK, WM, WN, NS>;
   using V8 = typename Frag<T>::type;
   constexpr int NT = G::NT, NW = G::NW, WTM = G::WTM, WTN = G::WTN, FM = G::FM, FN = G::FN;
   constexpr int KCH = G::KCH, NCH = G::NCH, A_CH = G::A_CH, B_CH = G::B_CH;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * G::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[G::SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -251,18 +268,22 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   // LDS stage (lane L -> bytes 16L..16L+15).  The swizzled layout is made by
   // choosing which global chunk each lane fetches: the lane that owns LDS
   // chunk slot `phys` of row r fetches logical chunk phys ^ swizzle(r).
+  // Offsets are relative to the slab's first k; an offset with bit 31 set
+  // is past the 2^31 - 1 byte buffer range and reads zero.  tail_bits has
+  // bit j set when load j lies beyond K in the last slab.
+  const int KT = (K + BK - 1) / BK;
+  const int k_last = (KT - 1) * BK;
+  uint32_t tail_bits = 0;
   uint32_t a_off[A_CH];
-  int a_k[A_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int blk = i * NW + wave;
     const int r = blk * G::A_RPB + lane / KCH;
     const int kc = (lane % KCH) ^ G::swz_k(r);
     a_off[i] = (m0 + r < M) ? (uint32_t)((r * p.lda + kc * 8) * 2) : kOOB;
-    a_k[i] = kc * 8;
+    if (k_last + kc * 8 >= K) tail_bits |= 1u << i;
   }
   uint32_t b_off[B_CH];
-  int b_k[B_CH];
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
     const int blk = i * NW + wave;
@@ -270,40 +291,42 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       const int r = blk * G::A_RPB + lane / KCH;
       const int kc = (lane % KCH) ^ G::swz_k(r);
       b_off[i] = (n0 + r < N) ? (uint32_t)((r * p.ldb + kc * 8) * 2) : kOOB;
-      b_k[i] = kc * 8;
+      if (k_last + kc * 8 >= K) tail_bits |= 1u << (A_CH + i);
     } else {             // B stored [K,N]: rows are k
       const int kr = blk * G::B_RPB + lane / NCH;
       const int nc = (lane % NCH) ^ G::swz_n(kr);
       b_off[i] = (n0 + nc * 8 < N) ? (uint32_t)((kr * p.ldb + nc * 8) * 2) : kOOB;
-      b_k[i] = kr;
+      if (k_last + kr >= K) tail_bits |= 1u << (A_CH + i);
     }
   }
 
   const uint8_t* Abase = (const uint8_t*)p.A + (size_t)m0 * p.lda * 2;
   const uint8_t* Bbase = BT ? (const uint8_t*)p.B + (size_t)n0 * p.ldb * 2
                             : (const uint8_t*)p.B + (size_t)n0 * 2;
-  const int KT = (K + BK - 1) / BK;
-  const bool ktail = (K % BK) != 0;
 
-  auto issue = [&](int kt, uint8_t* st) {
+  // load j (0 <= j < LPS) of this wave's share of slab kt into stage st:
+  // j < A_CH are A blocks, the rest B blocks.  A slab kt >= KT is a
+  // placeholder: its loads read nothing and write zeros into a stage that
+  // no later slab uses, which keeps the count of loads per slab uniform.
+  auto issue_one = [&](int kt, uint8_t* st, int j) {
     const uint32_t st_addr = __builtin_amdgcn_readfirstlane(lds_addr_of(st));
-    const int k0 = kt * BK;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (size_t)k0 * 2);
-    const __amdgpu_buffer_rsrc_t rB =
-        BT ? make_rsrc(Bbase + (size_t)k0 * 2) : make_rsrc(Bbase + (size_t)k0 * p.ldb * 2);
-    const bool last = ktail && (kt == KT - 1);
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      uint32_t off = a_off[i];
-      if (last && k0 + a_k[i] >= K) off = kOOB;
-      buffer_load16_lds(rA, st_addr + (i * NW + wave) * 1024, off);
+    const bool none = kt >= KT;
+    const int k0 = none ? 0 : kt * BK;
+    // branch-free: bit 31 from "placeholder" (uniform) or "beyond K" (lane)
+    const uint32_t kill = (none ? kOOB : 0u) | ((kt == KT - 1 ? (tail_bits >> j) & 1u : 0u) << 31);
+    if (j < A_CH) {
+      const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (size_t)k0 * 2);
+      buffer_load16_lds(rA, st_addr + (j * NW + wave) * 1024, a_off[j] | kill);
+    } else {
+      const int i = j - A_CH;
+      const __amdgpu_buffer_rsrc_t rB =
+          BT ? make_rsrc(Bbase + (size_t)k0 * 2) : make_rsrc(Bbase + (size_t)k0 * p.ldb * 2);
+      buffer_load16_lds(rB, st_addr + G::A_BYTES + (i * NW + wave) * 1024, b_off[i] | kill);
     }
+  };
+  auto issue = [&](int kt, uint8_t* st) {
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      uint32_t off = b_off[i];
-      if (last && k0 + b_k[i] >= K) off = kOOB;
-      buffer_load16_lds(rB, st_addr + G::A_BYTES + (i * NW + wave) * 1024, off);
-    }
+    for (int j = 0; j < G::LPS; ++j) issue_one(kt, st, j);
   };
 
   f32x16 acc[FM][FN];
@@ -317,35 +340,73 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   const int lrow = lane & 31;   // row (A) / column (B) within a 32x32 MFMA tile
   const int khalf = lane >> 5;  // which 8-wide k group of a 16-wide step
 
+  // A fragment (rows of A) and B fragment (columns of B) of k step ks of
+  // the slab at sA.  The per-lane LDS offsets are computed once: fragment fm
+  // (fn) and k step ks only add constants, because the swizzles repeat
+  // every 32 K-contiguous rows and every 16 N-contiguous k rows.
+  constexpr int KS = BK / 16;
+  static_assert((32 / G::RPK) % KCH == 0, "A/B_T swizzle must repeat every 32 rows");
+  static_assert((4 * (16 / G::RPN)) % NCH == 0, "B swizzle must repeat every 16 k rows");
+  uint32_t a_lds[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int r = wm * WTM + lrow;
+    a_lds[ks] = (uint32_t)(r * BK * 2 + (((ks * 2 + khalf) ^ G::swz_k(r)) << 4));
+  }
+  constexpr int BL = BT ? KS : 2 * FN;
+  uint32_t b_lds[BL];
+  if constexpr (BT) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int r = wn * WTN + lrow;
+      b_lds[ks] = (uint32_t)(G::A_BYTES + r * BK * 2 + (((ks * 2 + khalf) ^ G::swz_k(r)) << 4));
+    }
+  } else {
+    // two transposing reads per fragment: lane (g, i) = (lane / 16, lane % 16)
+    // reads k rows 8 (g / 2) + i / 4 (+ 4), columns 16 (g % 2) + 4 (i % 4) ..
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int ncol = wn * WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
+      const int nc = ncol >> 3, nb = (ncol & 7) * 2;
+      const int kr0 = (g >> 1) * 8 + (i >> 2), kr1 = kr0 + 4;
+      b_lds[2 * fn] = (uint32_t)(G::A_BYTES + kr0 * BN * 2 + ((nc ^ G::swz_n(kr0)) << 4) + nb);
+      b_lds[2 * fn + 1] = (uint32_t)(G::A_BYTES + kr1 * BN * 2 + ((nc ^ G::swz_n(kr1)) << 4) + nb);
+    }
+  }
+  auto read_a = [&](const uint8_t* sA, int ks, int fm) -> V8 {
+    return *(const V8*)(sA + a_lds[ks] + fm * 32 * BK * 2);
+  };
+  auto read_b = [&](const uint8_t* sA, int ks, int fn) -> V8 {
+    if constexpr (BT) {
+      return *(const V8*)(sA + b_lds[ks] + fn * 32 * BK * 2);
+    } else {
+      const u32x2 lo = lds_read_tr(sA + b_lds[2 * fn] + ks * 16 * BN * 2, T{});
+      const u32x2 hi = lds_read_tr(sA + b_lds[2 * fn + 1] + ks * 16 * BN * 2, T{});
+      const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+      return __builtin_bit_cast(V8, w);
+    }
+  };
+
+  // the FM x FN MFMAs of one k step; between(q) is placed after MFMA q
+  auto mfma_step = [&](const V8 (&af)[FM], const V8 (&bf)[FN], auto&& between) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        acc[fm][fn] = mfma32(bf[fn], af[fm], acc[fm][fn]);
+        between(fm * FN + fn);
+      }
+  };
+
   auto compute = [&](const uint8_t* sA) {
-    const uint8_t* sB = sA + G::A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       V8 af[FM], bf[FN];
-      const int kc = ks * 2 + khalf;
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        const int r = wm * WTM + fm * 32 + lrow;
-        af[fm] = *(const V8*)(sA + r * BK * 2 + ((kc ^ G::swz_k(r)) << 4));
-      }
+      for (int fm = 0; fm < FM; ++fm) af[fm] = read_a(sA, ks, fm);
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        if constexpr (BT) {
-          const int r = wn * WTN + fn * 32 + lrow;
-          bf[fn] = *(const V8*)(sB + r * BK * 2 + ((kc ^ G::swz_k(r)) << 4));
-        } else {
-          // two transposing reads: k = ks*16 + 8*(lane/32) + {0..3, 4..7}
-          const int g = lane >> 4, i = lane & 15;
-          const int ncol = wn * WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
-          const int nc = ncol >> 3, nb = (ncol & 7) * 2;
-          const int kr0 = ks * 16 + (g >> 1) * 8 + (i >> 2);
-          const int kr1 = kr0 + 4;
-          const u32x2 lo = lds_read_tr(sB + kr0 * BN * 2 + ((nc ^ G::swz_n(kr0)) << 4) + nb, T{});
-          const u32x2 hi = lds_read_tr(sB + kr1 * BN * 2 + ((nc ^ G::swz_n(kr1)) << 4) + nb, T{});
-          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          bf[fn] = __builtin_bit_cast(V8, w);
-        }
-      }
+      for (int fn = 0; fn < FN; ++fn) bf[fn] = read_b(sA, ks, fn);
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -353,17 +414,60 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     }
   };
 
-  // prologue: slabs 0 .. NS-2 in flight, wait for slab 0
+  // prologue: slabs 0 .. NS-2 (or placeholders) in flight, wait for slab 0
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < KT) issue(s, smem + s * G::STAGE);
-  if (KT >= NS - 1)
-    wait_vmcnt<(NS - 2) * G::LPS>();
-  else
-    wait_vmcnt<0>();
+  for (int s = 0; s < NS - 1; ++s) issue(s, smem + s * G::STAGE);
+  wait_vmcnt<(NS - 2) * G::LPS>();
   __syncthreads();
   int cur = 0;                      // stage of slab kt
   int nxt = NS - 1;                 // stage that receives slab kt + NS - 1
+  if constexpr (SCHED == 1) {
+    // Ping-pong.  Waves w and w + 4 of the workgroup share a SIMD; they are
+    // in the two groups grp = w / 4.  Each wave alternates a load phase -- read
+    // all of its fragments of slab kt into registers, wait for its share of
+    // slab kt + 1 -- and a compute phase of FM * FN * BK / 16 MFMAs on
+    // registers, between which it issues its share of the slab NS - 1
+    // ahead.  Group 1 starts one phase late, so while one group multiplies
+    // the other loads, and the barrier that ends a phase only hands the
+    // matrix cores over.  Slab s is read in phases 2s (group 0) and 2s + 1
+    // (group 1); its stage is refilled (slab s + NS) from phase 2s + 3 on
+    // and read again in phase 2s + 2 NS, after both groups' waits for it.
+    const int grp = wave >> 2;
+    if (grp == 1) phase_barrier();
+    for (int kt = 0; kt < KT; ++kt) {
+      V8 af[KS][FM], bf[KS][FN];
+      const uint8_t* st = smem + cur * G::STAGE;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) af[ks][fm] = read_a(st, ks, fm);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) bf[ks][fn] = read_b(st, ks, fn);
+      }
+      // own share of slab kt + 1 landed: slabs (or placeholders) up to
+      // kt + NS - 2 were issued, in the prologue and the compute phases
+      // before this one, LPS loads each
+      wait_vmcnt<(NS - 3) * G::LPS>();
+      phase_barrier();
+      // compute phase; it also refills the stage of slab kt - 1 (released
+      // by both groups' load phases) with slab kt + NS - 1, one load after
+      // each of the first LPS MFMAs
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        mfma_step(af[ks], bf[ks], [&](int q) {
+          const int d = ks * FM * FN + q;
+          if (d < G::LPS) issue_one(kt + NS - 1, smem + nxt * G::STAGE, d);
+        });
+      phase_barrier();
+      cur = (cur + 1 == NS) ? 0 : cur + 1;
+      nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
+    }
+    if (grp == 0) phase_barrier();
+    // the placeholder loads of the last compute phases write into the ring,
+    // which the epilogue reuses
+    wait_vmcnt<0>();
+    __syncthreads();
+  } else
   for (int kt = 0; kt < KT; ++kt) {
     // the stage of slab kt-1 is free: every wave passed the last barrier
     const bool more = kt + NS - 1 < KT;
@@ -380,28 +484,25 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   }
 
   // ---- epilogue on the accumulators -----------------------------------------
-  // lane owns row m = wrow0 + 32 fm + lrow and, in tile (fm, fn), columns
-  // cgrp + 8 g + {0,1,2,3} for g = 0..3 (elements r = 4 g + e).
+  // lane owns local row rl = wrow0 + 32 fm + lrow and, in tile (fm, fn), the
+  // columns cl + 8 g + {0,1,2,3} (g = 0..3, elements r = 4 g + e) with
+  // cl = wcol0 + 32 fn + 4 khalf.  The results are rounded into an LDS copy
+  // of the output tile (free since the main loop's last barrier) and then
+  // written to HBM row by row with 16-byte stores: written straight from the
+  // accumulator layout, every store instruction would touch 64 rows.
   const int epi = p.epi;
-  const int wrow0 = m0 + wm * WTM;
-  const int wcol0 = n0 + wn * WTN;
-  const size_t ldo = (size_t)p.ldo;
-  const bool vec_store = (p.ldo & 3) == 0;  // 8-byte aligned 4-column groups
+  const int wrow0 = wm * WTM;
+  const int wcol0 = wn * WTN;
+  uint8_t* const so = smem;                                  // [BM][BN] of T
+  float* const red = (float*)(smem + G::OUT_BYTES);          // [WM][BN] fp32
 
-  auto store_tile = [&](int m, int cgrp, const float (&y)[16]) {
-    if (m >= M) return;
-    T* orow = (T*)p.out + (size_t)m * ldo;
+  auto stage = [&](int rl, int cl, const float (&y)[16]) {
+    uint8_t* row = so + rl * (BN * 2) + (cl & 7) * 2;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int c = cgrp + 8 * g;
-      if (vec_store && c + 3 < N) {
-        u32x2 w = {pack2(y[4 * g], y[4 * g + 1], T{}), pack2(y[4 * g + 2], y[4 * g + 3], T{})};
-        *(u32x2*)(orow + c) = w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c + e < N) orow[c + e] = from_f32<T>(y[4 * g + e]);
-      }
+      const int c = cl + 8 * g;
+      const u32x2 w = {pack2(y[4 * g], y[4 * g + 1], T{}), pack2(y[4 * g + 2], y[4 * g + 3], T{})};
+      *(u32x2*)(row + (((c >> 3) ^ G::swz_o(rl)) << 4)) = w;
     }
   };
 
@@ -414,10 +515,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       for (int r = 0; r < 16; ++r) cs[fn][r] = 0.0f;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
-      const int m = wrow0 + fm * 32 + lrow;
+      const int rl = wrow0 + fm * 32 + lrow;
+      const int m = m0 + rl;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int cbase = wcol0 + fn * 32;
+        const int cbase = n0 + wcol0 + fn * 32;
         const uint32_t mw = (m < M && cbase < N)
                                 ? p.aux[(size_t)m * p.aux_ld + (cbase >> 5)] >> (4 * khalf)
                                 : 0u;
@@ -428,7 +530,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           y[r] = ((mw >> bit) & 1u) ? acc[fm][fn][r] : 0.0f;
           cs[fn][r] += y[r];
         }
-        store_tile(m, cbase + 4 * khalf, y);
+        stage(rl, wcol0 + fn * 32 + 4 * khalf, y);
       }
     }
     // sum over the 32 rows held by the lanes with the same khalf
@@ -444,7 +546,6 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         v += __shfl_xor(v, 16);
         cs[fn][r] = v;
       }
-    float* red = (float*)smem;  // [WM][BN] column sums per wave row
     if (lrow == 0) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
@@ -452,65 +553,97 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         for (int r = 0; r < 16; ++r)
           red[wm * BN + wn * WTN + fn * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3)] = cs[fn][r];
     }
-    __syncthreads();
+  } else {
+    const bool has_bias = epi != EPI_DEFAULT;
+    const bool per_col = p.bias_per_col != 0;
+    const T* bias = (const T*)p.bias;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int rl = wrow0 + fm * 32 + lrow;
+      const int m = m0 + rl;
+      const float brow = (has_bias && !per_col && m < M) ? to_f32(bias[m]) : 0.0f;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int cbase = n0 + wcol0 + fn * 32;
+        const int cgrp = cbase + 4 * khalf;
+        float y[16];
+        uint32_t bits = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = cgrp + 8 * (r >> 2) + (r & 3);
+          float b = brow;
+          if (has_bias && per_col) b = c < N ? to_f32(bias[c]) : 0.0f;
+          const float z = acc[fm][fn][r] + b;
+          if (epi == EPI_GELU_BIAS) {
+            y[r] = gelu_erf(z);
+          } else if (epi == EPI_RELU_BIAS || epi == EPI_RELU_AUX_BIAS) {
+            y[r] = z > 0.0f ? z : 0.0f;
+          } else {
+            y[r] = z;
+          }
+          if (epi == EPI_RELU_AUX_BIAS && z > 0.0f && c < N)
+            bits |= 1u << (8 * (r >> 2) + 4 * khalf + (r & 3));
+        }
+        stage(rl, wcol0 + fn * 32 + 4 * khalf, y);
+        if (epi == EPI_RELU_AUX_BIAS) {
+          // lanes l and l+32 hold complementary halves of row m's word
+          bits |= __shfl_xor(bits, 32);
+          if (khalf == 0 && m < M && cbase < N) {
+            uint32_t* mrow = p.aux + (size_t)m * p.aux_ld;
+            const int word = cbase >> 5;
+            mrow[word] = bits;
+            if (word == p.aux_words - 1)
+              for (int w = p.aux_words; w < p.aux_ld; ++w) mrow[w] = 0u;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // the staged tile -> out: thread t copies 16-byte chunk t % CPR of local
+  // row t / CPR (+ RPP per pass), so a wave writes whole row segments
+  constexpr int CPR = BN / 8, RPP = NT / CPR;
+  const size_t ldo = (size_t)p.ldo;
+  const bool vec_store = (p.ldo & 7) == 0;  // 16-byte aligned rows
+  const int ch = tid % CPR;
+  const int n = n0 + ch * 8;
+#pragma unroll 4
+  for (int rl = tid / CPR; rl < BM; rl += RPP) {
+    const u32x4 v = *(const u32x4*)(so + rl * (BN * 2) + ((ch ^ G::swz_o(rl)) << 4));
+    const int m = m0 + rl;
+    if (m >= M || n >= N) continue;
+    T* dst = (T*)p.out + (size_t)m * ldo + n;
+    if (vec_store && n + 7 < N) {
+      *(u32x4*)dst = v;
+    } else {
+      uint16_t* d16 = (uint16_t*)dst;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) d16[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+
+  if (epi == EPI_DRELU_BGRAD) {
     for (int c = tid; c < BN; c += NT) {
       float s = 0.0f;
 #pragma unroll
       for (int w = 0; w < WM; ++w) s += red[w * BN + c];
       if (n0 + c < N) unsafeAtomicAdd(&p.bgrad[n0 + c], s);
     }
-    return;
-  }
-
-  const bool has_bias = epi != EPI_DEFAULT;
-  const bool per_col = p.bias_per_col != 0;
-  const T* bias = (const T*)p.bias;
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = wrow0 + fm * 32 + lrow;
-    const float brow = (has_bias && !per_col && m < M) ? to_f32(bias[m]) : 0.0f;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int cbase = wcol0 + fn * 32;
-      const int cgrp = cbase + 4 * khalf;
-      float y[16];
-      uint32_t bits = 0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = cgrp + 8 * (r >> 2) + (r & 3);
-        float b = brow;
-        if (has_bias && per_col) b = c < N ? to_f32(bias[c]) : 0.0f;
-        const float z = acc[fm][fn][r] + b;
-        if (epi == EPI_GELU_BIAS) {
-          y[r] = gelu_erf(z);
-        } else if (epi == EPI_RELU_BIAS || epi == EPI_RELU_AUX_BIAS) {
-          y[r] = z > 0.0f ? z : 0.0f;
-        } else {
-          y[r] = z;
-        }
-        if (epi == EPI_RELU_AUX_BIAS && z > 0.0f && c < N)
-          bits |= 1u << (8 * (r >> 2) + 4 * khalf + (r & 3));
-      }
-      store_tile(m, cgrp, y);
-      if (epi == EPI_RELU_AUX_BIAS) {
-        // lanes l and l+32 hold complementary halves of row m's word
-        bits |= __shfl_xor(bits, 32);
-        if (khalf == 0 && m < M && cbase < N) {
-          uint32_t* mrow = p.aux + (size_t)m * p.aux_ld;
-          const int word = cbase >> 5;
-          mrow[word] = bits;
-          if (word == p.aux_words - 1)
-            for (int w = p.aux_words; w < p.aux_ld; ++w) mrow[w] = 0u;
-        }
-      }
-    }
   }
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT, int SCHED>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
+  static_assert(SCHED == 0 || SCHED == 1, "schedule");
+  static_assert(SCHED != 1 || WM * WN == 8, "ping-pong pairs waves w and w + 4 on each SIMD");
+  static_assert(SCHED != 1 || NS >= 3, "ping-pong issues each slab NS - 1 ahead from a compute phase");
+  static_assert(SCHED != 1 || (BK / 16) * (BM / WM / 32) * (BN / WN / 32) >=
+                                  GemmTile<BM, BN, BK, WM, WN, NS>::LPS,
+                "ping-pong issues one load after each MFMA of a compute phase");
   const int blocks = a.tiles_m * a.tiles_n;
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, NS, BT>), dim3(blocks), dim3(WM * WN * 64),
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, NS, BT, SCHED>), dim3(blocks), dim3(WM * WN * 64),
                      0, s, a);
   return hipGetLastError();
 }
@@ -518,9 +651,9 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 template <typename T, bool BT>
 hipError_t launch_by_tile(int tile, const GemmArgs& a, hipStream_t s) {
   switch (tile) {
-#define GEMMEPI_CASE(id, bm, bn, bk, wm, wn, ns) \
-  case id:                                       \
-    return launch_tile<T, bm, bn, bk, wm, wn, ns, BT>(a, s);
+#define GEMMEPI_CASE(id, bm, bn, bk, wm, wn, ns, pp) \
+  case id:                                           \
+    return launch_tile<T, bm, bn, bk, wm, wn, ns, BT, pp>(a, s);
     GEMMEPI_TILES(GEMMEPI_CASE)
 #undef GEMMEPI_CASE
     default:

@@ -27,8 +27,8 @@
 
 namespace gemmepi {
 
-#define GEMMEPI_TILE_ENTRY(id, bm, bn, bk, wm, wn, ns) \
-  {bm, bn, bk, wm, wn, ns, #bm "x" #bn "x" #bk "_w" #wm "x" #wn "_s" #ns},
+#define GEMMEPI_TILE_ENTRY(id, bm, bn, bk, wm, wn, ns, sched) \
+  {bm, bn, bk, wm, wn, ns, sched, #bm "x" #bn "x" #bk "_w" #wm "x" #wn "_s" #ns "_p" #sched},
 const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 #undef GEMMEPI_TILE_ENTRY
 
@@ -38,8 +38,8 @@ const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 // kNumCU * occ tiles; in one round a CU holds up to `occ` tiles that share
 // its MFMA units, so
 //   est = rounds * min(occ, ceil(tiles / kNumCU)) * BM * BN / eff.
-static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.86, 0.82, 0.70, 0.66, 0.56};
-static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 1, 2, 3};
+static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.86, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95};
+static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 1, 2, 3, 1, 1};
 constexpr int kNumCU = 256;
 
 hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s) {

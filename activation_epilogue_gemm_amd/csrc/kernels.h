@@ -57,11 +57,11 @@ struct DecodeArgs {
 
 // One tile configuration of the tiled GEMM.
 struct TileCfg {
-  int bm, bn, bk, wm, wn, ns;
+  int bm, bn, bk, wm, wn, ns, sched;
   const char* name;
 };
 
-constexpr int kNumTiles = 7;
+constexpr int kNumTiles = 9;
 extern const TileCfg kTiles[kNumTiles];
 
 // Launchers (defined in the per-dtype/per-layout instantiation files).

@@ -66,11 +66,17 @@ def run_and_check(c, flags=0, tile=-1, exact=False, guard=0, label=""):
 
 
 # ---------------------------------------------------------------- every tile, exact
-@pytest.mark.parametrize("tile", range(7))
+NUM_TILES = 9
+
+
+def test_tile_count():
+    assert ge.num_tiles() == NUM_TILES
+
+
+@pytest.mark.parametrize("tile", range(NUM_TILES))
 @pytest.mark.parametrize("b_trans", [False, True])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_integer_exact_every_tile(tile, b_trans, dtype):
-    assert ge.num_tiles() == 7
     M, N, K = 300, 264, 200   # ragged in M, N and K for every tile shape
     for ei, epi in enumerate(EPIS):
         if epi == "GELU_BIAS":
@@ -81,9 +87,14 @@ def test_integer_exact_every_tile(tile, b_trans, dtype):
             c = wl.random_case(M, N, K, dtype, epi, b_trans, per_col, 100 + 7 * ei + per_col,
                                kind="int")
             run_and_check(c, tile=tile, exact=True, guard=64, label=f"tile{tile}")
+    # fewer k slabs than pipeline stages, and a single partial slab
+    for K in (8, 72):
+        c = wl.random_case(70, 40, K, dtype, "RELU_AUX_BIAS", b_trans, b_trans, 900 + K,
+                           kind="int")
+        run_and_check(c, tile=tile, exact=True, guard=64, label=f"tile{tile} K={K}")
 
 
-@pytest.mark.parametrize("tile", range(7))
+@pytest.mark.parametrize("tile", range(NUM_TILES))
 @pytest.mark.parametrize("b_trans", [False, True])
 def test_tolerance_every_tile_gelu_and_normal_inputs(tile, b_trans):
     M, N, K = 260, 200, 328

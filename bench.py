@@ -195,7 +195,9 @@ def cpu_baseline(seconds_target=12.0):
                         "RELU_AUX_BIAS", False, False)
         return time.perf_counter() - t
     run(rows_all[:32])
-    probe = 512
+    # fp64 matmul throughput still rises with the row count at this size,
+    # so the probe is large (about a second) and the estimate conservative
+    probe = 4096
     dt = run(rows_all[:probe])
     nrows = int(max(probe, min(len(rows_all), probe * seconds_target / max(dt, 1e-3))))
     rows = rows_all[:nrows]

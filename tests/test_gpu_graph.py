@@ -1,0 +1,75 @@
+"""Graph capture of execute(): a captured execution, replayed several times
+with new inputs copied into the captured buffers and eager work and
+synchronisations in between, must match an eager execution of the same
+plan bit for bit.  Integer inputs make every fp32 sum exact, so this holds
+for the bias gradient too, whatever the order of its atomic additions.
+DRELU_BGRAD exercises the zero-fill kernel that precedes the GEMM (a fill
+kernel, not a memset node, so that replays re-zero the gradient)."""
+import numpy as np
+import pytest
+
+import activation_epilogue_gemm_amd as ge
+import workloads as wl
+from parity import download_bits, flags_of, torch_dtype, upload_bits, upload_words
+
+pytestmark = pytest.mark.gpu
+
+
+def _buffers(c):
+    import torch
+    d = {"A": upload_bits(c.A, c.dtype), "B": upload_bits(c.B, c.dtype),
+         "out": torch.empty(c.M, c.N, dtype=torch_dtype(c.dtype), device="cuda")}
+    if c.epilogue == "DRELU_BGRAD":
+        d["bias"] = torch.empty(c.N, dtype=torch.float32, device="cuda")
+        d["aux"] = upload_words(c.aux)
+    else:
+        d["bias"] = upload_bits(c.bias, c.dtype)
+        d["aux"] = torch.zeros(c.M, ge.aux_ld_words(c.N), dtype=torch.int32, device="cuda")
+    return d
+
+
+@pytest.mark.parametrize("epi,b_trans,tile", [
+    ("RELU_AUX_BIAS", False, -1),
+    ("DRELU_BGRAD", False, -1),
+    ("GELU_BIAS", True, 7),
+    ("BIAS", True, 8),
+])
+def test_graph_replays_match_eager(epi, b_trans, tile):
+    import torch
+    M, N, K = 520, 392, 264
+    cases = [wl.random_case(M, N, K, "f16", epi, b_trans, b_trans, 4000 + 17 * r, kind="int")
+             for r in range(4)]
+    flags = flags_of(cases[0])
+    with ge.plan(M, N, K, "f16", epi, flags, tile=tile) as p:
+        cap = _buffers(cases[0])
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            p.execute(cap["A"], cap["B"], cap["bias"], cap["aux"], cap["out"])  # warm-up
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            p.execute(cap["A"], cap["B"], cap["bias"], cap["aux"], cap["out"])
+        for r, c in enumerate(cases):
+            new = _buffers(c)
+            for k in ("A", "B"):
+                cap[k].copy_(new[k])
+            if epi == "DRELU_BGRAD":
+                cap["aux"].copy_(new["aux"])
+                cap["bias"].fill_(777.0)          # replay must overwrite, not accumulate
+            else:
+                cap["bias"].copy_(new["bias"])
+            cap["out"].fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            # eager execution of the same plan on separate buffers
+            p.execute(new["A"], new["B"], new["bias"], new["aux"], new["out"])
+            torch.cuda.synchronize()
+            assert np.array_equal(download_bits(cap["out"]), download_bits(new["out"])), f"replay {r}: out"
+            if epi == "RELU_AUX_BIAS":
+                assert torch.equal(cap["aux"], new["aux"]), f"replay {r}: mask"
+            if epi == "DRELU_BGRAD":
+                assert torch.equal(cap["bias"], new["bias"]), f"replay {r}: bgrad"
+        del g

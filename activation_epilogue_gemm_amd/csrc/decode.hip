@@ -66,17 +66,18 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
   const int Mt = p.M;
   const int epi = p.epi;
 
-  // the epilogue's bias values, fetched before the weight stream so their
-  // latency is hidden (lane: token t = r16, columns n0 + 4 kg + r)
-  const T* bias = (const T*)p.bias;
-  float bv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (epi != EPI_DEFAULT && r16 < Mt) {
+  // The epilogue's bias values (lane: token t = r16, columns n0 + 4 kg + r)
+  // are requested up front and converted only in the epilogue, so no wait
+  // for them delays the weight stream.  Out-of-range entries read zero.
+  const __amdgpu_buffer_rsrc_t rBias = make_rsrc(p.bias ? p.bias : p.W);
+  const bool want_bias = epi != EPI_DEFAULT && r16 < Mt;
+  uint16_t braw[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = n0 + kg * 4 + r;
-      if (p.bias_per_col) bv[r] = n < p.N ? to_f32(bias[n]) : 0.0f;
-      else bv[r] = to_f32(bias[r16]);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int n = n0 + kg * 4 + r;
+    const bool ok = want_bias && (p.bias_per_col ? n < p.N : true);
+    const uint32_t off = ok ? (uint32_t)(p.bias_per_col ? n : r16) * 2u : kOOB;
+    braw[r] = __builtin_amdgcn_raw_buffer_load_b16(rBias, off, 0, 0);
   }
 
   const __amdgpu_buffer_rsrc_t rW = make_rsrc((const uint8_t*)p.W + (size_t)n0 * p.ldw * 2);
@@ -129,7 +130,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
   for (int r = 0; r < 4; ++r) {
     const int n = n0 + kg * 4 + r;
     if (n >= p.N) continue;
-    const float z = s[r] + bv[r];
+    const float z = s[r] + to_f32(__builtin_bit_cast(T, braw[r]));
     float y = z;
     if (epi == EPI_GELU_BIAS) y = gelu_erf(z);
     else if (epi == EPI_RELU_BIAS) y = z > 0.0f ? z : 0.0f;

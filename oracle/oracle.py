@@ -40,6 +40,20 @@ Readings where the pages are silent (each listed in the design notes):
     rounded up to a multiple of 4; column j of row i is bit (j & 31) of word
     (i, j >> 5); padding bits are 0.
 
+Structural fusion (ops-nn MatMul fusion article, section "Level 2:
+structural fusion": MatMul + bias + residual + LayerNorm/RMSNorm as one
+operator) is in gemm_norm():
+
+    y[i,:]   = acc[i,:] + bias[:] + residual[i,:]     fp64
+    LAYERNORM  out = (y - mean(y)) / sqrt(var(y) + eps) * gamma + beta
+    RMSNORM    out = y / sqrt(mean(y^2) + eps) * gamma
+    mean/var over the N columns of a row; var is the biased (1/N) variance
+
+with the readings: the residual is added to the GEMM result before the
+normalisation (post-norm order); eps sits inside the square root; gamma,
+beta and bias are per column.  The page names the operator but prints no
+formula; these are the standard definitions of the two norms.
+
 Pins: tests/test_oracle_pins.py checks this module against brute-force
 exact sums (math.fsum over exactly-represented products, Fraction-based
 rounding), exact integer arithmetic, closed-form GELU values, invariants of
@@ -54,6 +68,7 @@ from typing import Optional
 import numpy as np
 
 EPILOGUES = ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "DRELU_BGRAD")
+NORMS = ("RMSNORM", "LAYERNORM")
 
 
 # --------------------------------------------------------------------------
@@ -245,3 +260,55 @@ def ffn_block(x, W1, b1, W2, b2, tokens: int, hidden: int, inter: int, dtype: st
     h = gemm_epilogue(x, W1, b1, None, tokens, inter, hidden, dtype, "GELU_BIAS", True, True)
     y = gemm_epilogue(h.out, W2, b2, None, tokens, hidden, inter, dtype, "BIAS", True, True)
     return h, y
+
+
+@dataclass
+class NormResult:
+    rows: np.ndarray                 # which output rows were computed
+    out: np.ndarray                  # storage bits [R, N] (uint16)
+    y: np.ndarray                    # fp64 acc + bias + residual [R, N]
+    mean: np.ndarray                 # fp64 row mean of y [R] (RMSNORM: 0)
+    rstd: np.ndarray                 # fp64 1 / sqrt(var + eps) (RMSNORM: of mean(y^2))
+    out64: np.ndarray                # fp64 normalised value before rounding [R, N]
+
+
+def gemm_norm(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
+              residual: Optional[np.ndarray], gamma: np.ndarray, beta: Optional[np.ndarray],
+              eps: float, M: int, N: int, K: int, dtype: str, norm: str, b_trans: bool,
+              rows: Optional[np.ndarray] = None) -> NormResult:
+    """Reference of the GEMM + bias + residual + row-norm operator (ops-nn
+    MatMul fusion article, section "Level 2: structural fusion").
+
+    A: storage bits [M, K]; B: [K, N], or [N, K] with ``b_trans``; bias,
+    gamma, beta: [N] storage bits (bias and beta may be None: zero);
+    residual: [M, N] storage bits or None.  Every row is normalised over all
+    N of its columns; ``rows`` selects the rows computed and returned.
+    """
+    if norm not in NORMS:
+        raise ValueError(norm)
+    A64 = decode(np.asarray(A).reshape(M, K), dtype)
+    B64 = decode(np.asarray(B).reshape((N, K) if b_trans else (K, N)), dtype)
+    if b_trans:
+        B64 = B64.T
+    rows = np.arange(M) if rows is None else np.asarray(rows)
+    y = A64[rows] @ B64                                # [R, N]
+    if bias is not None:
+        y = y + decode(np.asarray(bias), dtype)[None, :N]
+    if residual is not None:
+        y = y + decode(np.asarray(residual).reshape(M, N), dtype)[rows]
+    g = decode(np.asarray(gamma), dtype)[None, :N]
+    if norm == "LAYERNORM":
+        mean = y.mean(axis=1)
+        d = y - mean[:, None]
+        var = (d * d).mean(axis=1)                     # two-pass, biased
+        rstd = 1.0 / np.sqrt(var + eps)
+        out64 = d * rstd[:, None] * g
+        if beta is not None:
+            out64 = out64 + decode(np.asarray(beta), dtype)[None, :N]
+    else:
+        mean = np.zeros(len(rows))
+        ms = (y * y).mean(axis=1)
+        rstd = 1.0 / np.sqrt(ms + eps)
+        out64 = y * rstd[:, None] * g
+    return NormResult(rows=rows, out=encode(out64, dtype), y=y, mean=mean, rstd=rstd,
+                      out64=out64)

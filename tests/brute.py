@@ -117,3 +117,41 @@ def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
     if epilogue == "DRELU_BGRAD":
         bgrad = [f32_round(math.fsum(t)) for t in colsum_terms]
     return out, (mask if epilogue == "RELU_AUX_BIAS" else None), bgrad
+
+
+def norm(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
+         residual: Optional[Sequence[int]], gamma: Sequence[int], beta: Optional[Sequence[int]],
+         eps: float, M: int, N: int, K: int, dtype: str, kind: str, b_trans: bool):
+    """GEMM + bias + residual + row norm on tiny shapes; returns
+    (out_bits[M][N], out_values[M][N]).  y is the correctly rounded exact sum
+    of the products, the bias and the residual; the row statistics use
+    math.fsum as well."""
+    a = [[value(A[i * K + k], dtype) for k in range(K)] for i in range(M)]
+    if b_trans:
+        b = [[value(B[j * K + k], dtype) for j in range(N)] for k in range(K)]
+    else:
+        b = [[value(B[k * N + j], dtype) for j in range(N)] for k in range(K)]
+    g = [value(gamma[j], dtype) for j in range(N)]
+    bt = [value(beta[j], dtype) if beta is not None else 0.0 for j in range(N)]
+    bits, vals = [], []
+    for i in range(M):
+        y = []
+        for j in range(N):
+            terms = [a[i][k] * b[k][j] for k in range(K)]
+            if bias is not None:
+                terms.append(value(bias[j], dtype))
+            if residual is not None:
+                terms.append(value(residual[i * N + j], dtype))
+            y.append(math.fsum(terms))
+        if kind == "LAYERNORM":
+            mean = math.fsum(y) / N
+            var = math.fsum((v - mean) ** 2 for v in y) / N
+            rstd = 1.0 / math.sqrt(var + eps)
+            row = [(y[j] - mean) * rstd * g[j] + bt[j] for j in range(N)]
+        else:
+            ms = math.fsum(v * v for v in y) / N
+            rstd = 1.0 / math.sqrt(ms + eps)
+            row = [y[j] * rstd * g[j] for j in range(N)]
+        vals.append(row)
+        bits.append([out_bits(v, dtype) for v in row])
+    return bits, vals

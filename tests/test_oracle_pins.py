@@ -278,3 +278,99 @@ def test_ffn_chain_composes():
     yb, _, _ = brute.fused(np.array(hb, np.uint16).ravel().tolist(), W2.ravel().tolist(),
                            b2.tolist(), None, tok, H, I, "f16", "BIAS", True, True)
     assert y.out.tolist() == yb
+
+
+# ---------------------------------------------------------------- GEMM + residual + norm
+def test_norm_worked_example():
+    g = _golden("norm_example.json")
+    M, N, K = g["M"], g["N"], g["K"]
+    A = _f16(g["A"]).ravel()
+    B = _f16(g["B_KxN"]).ravel()
+    args = dict(bias=_f16(g["bias"]), residual=_f16(g["residual"]).ravel(),
+                gamma=_f16(g["gamma"]), beta=_f16(g["beta"]))
+    for kind, key in (("LAYERNORM", "layernorm"), ("RMSNORM", "rmsnorm")):
+        r = O.gemm_norm(A, B, args["bias"], args["residual"], args["gamma"],
+                        args["beta"] if kind == "LAYERNORM" else None, g[key]["eps"],
+                        M, N, K, "f16", kind, False)
+        assert np.array_equal(r.out64, np.asarray(g[key]["out"], dtype=np.float64)), kind
+        assert np.array_equal(r.out, _f16(g[key]["out"])), kind
+        assert np.array_equal(r.rstd, np.asarray(g[key]["rstd"])), kind
+        if kind == "LAYERNORM":
+            assert np.array_equal(r.mean, np.asarray(g[key]["mean"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("kind", ["LAYERNORM", "RMSNORM"])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_norm_brute_force_tiny(kind, dtype):
+    rng = np.random.default_rng(77)
+    for M, N, K, bt, with_bias, with_res in ((3, 5, 7, False, True, True), (2, 8, 4, True, True, False),
+                                             (4, 6, 9, True, False, True), (1, 3, 2, False, False, False)):
+        def draw(*shape, scale=1.0):
+            v = (rng.standard_normal(shape) * scale).astype(np.float32)
+            return wl.to_bits(v, dtype).ravel()
+        A = draw(M, K)
+        B = draw(N, K) if bt else draw(K, N)
+        bias = draw(N, scale=0.5) if with_bias else None
+        res = draw(M, N) if with_res else None
+        gamma = draw(N)
+        beta = draw(N, scale=0.3) if kind == "LAYERNORM" else None
+        eps = 1e-5
+        bits, vals = brute.norm(A, B, bias, res, gamma, beta, eps, M, N, K, dtype, kind, bt)
+        r = O.gemm_norm(A, B, bias, res, gamma, beta, eps, M, N, K, dtype, kind, bt)
+        assert np.allclose(r.out64, np.asarray(vals), rtol=1e-12, atol=1e-12)
+        assert np.array_equal(r.out, np.asarray(bits, dtype=np.uint16))
+
+
+def test_norm_closed_forms():
+    """Constant rows: LayerNorm gives beta exactly; RMSNorm gives
+    c / sqrt(c^2 + eps) * gamma."""
+    M, N, K = 3, 16, 4
+    A = _f16(np.zeros((M, K))).ravel()
+    B = _f16(np.ones((K, N))).ravel()
+    consts = np.array([1.5, -2.0, 0.0])
+    res = _f16(np.repeat(consts[:, None], N, axis=1)).ravel()
+    gamma = _f16(np.linspace(-1, 1, N))
+    beta = _f16(np.linspace(0.25, 2.0, N))
+    eps = 0.0625
+    ln = O.gemm_norm(A, B, None, res, gamma, beta, eps, M, N, K, "f16", "LAYERNORM", False)
+    assert np.array_equal(ln.out, np.tile(beta, (M, 1)))
+    rms = O.gemm_norm(A, B, None, res, gamma, None, eps, M, N, K, "f16", "RMSNORM", False)
+    g = O.decode(gamma, "f16")
+    want = consts[:, None] / np.sqrt(consts[:, None] ** 2 + eps) * g[None, :]
+    assert np.allclose(rms.out64, want, rtol=1e-15, atol=1e-15)
+
+
+def test_norm_invariants():
+    rng = np.random.default_rng(5)
+    M, N, K = 6, 40, 24
+    A = wl.to_bits(rng.standard_normal((M, K)).astype(np.float32), "f16").ravel()
+    B = wl.to_bits(rng.standard_normal((K, N)).astype(np.float32), "f16").ravel()
+    ones = _f16(np.ones(N))
+    zeros = _f16(np.zeros(N))
+    ln = O.gemm_norm(A, B, None, None, ones, zeros, 1e-3, M, N, K, "f16", "LAYERNORM", False)
+    y = ln.y
+    var = y.var(axis=1)
+    # normalised rows: mean 0, mean square var / (var + eps)
+    assert np.allclose(ln.out64.mean(axis=1), 0.0, atol=1e-12)
+    assert np.allclose((ln.out64 ** 2).mean(axis=1), var / (var + 1e-3), rtol=1e-12)
+    # shift invariance: a per-row constant in the residual changes nothing
+    shift = _f16(np.repeat(np.array([0.5, -4, 8, 0, 2, -1])[:, None], N, axis=1)).ravel()
+    ln2 = O.gemm_norm(A, B, None, shift, ones, zeros, 1e-3, M, N, K, "f16", "LAYERNORM", False)
+    assert np.allclose(ln2.out64, ln.out64, rtol=1e-9, atol=1e-9)
+    # RMSNorm: mean square of the output is ms / (ms + eps)
+    rms = O.gemm_norm(A, B, None, None, ones, None, 1e-3, M, N, K, "f16", "RMSNORM", False)
+    ms = (y * y).mean(axis=1)
+    assert np.allclose((rms.out64 ** 2).mean(axis=1), ms / (ms + 1e-3), rtol=1e-12)
+    # the GEMM part is the plain product: y equals the DEFAULT epilogue's value
+    d = O.gemm_epilogue(A, B, None, None, M, N, K, "f16", "DEFAULT", False, False)
+    assert np.array_equal(ln.y, d.y)
+    # bias and residual enter y additively, per column and per element
+    bias = _f16(np.linspace(-1, 1, N))
+    res = wl.to_bits(rng.standard_normal((M, N)).astype(np.float32), "f16").ravel()
+    both = O.gemm_norm(A, B, bias, res, ones, zeros, 1e-3, M, N, K, "f16", "LAYERNORM", False)
+    want = d.y + O.decode(bias, "f16")[None, :] + O.decode(res, "f16").reshape(M, N)
+    assert np.array_equal(both.y, want)
+    # rows select rows
+    sub = O.gemm_norm(A, B, bias, res, ones, zeros, 1e-3, M, N, K, "f16", "LAYERNORM", False,
+                      rows=np.array([4, 1]))
+    assert np.array_equal(sub.out, both.out[[4, 1]])

@@ -37,7 +37,8 @@ ERR_NO_MEMORY = 6
 
 DTYPES = {"f16": 0, "bf16": 1}
 EPILOGUES = {"DEFAULT": 0, "BIAS": 1, "RELU_BIAS": 2, "RELU_AUX_BIAS": 3, "GELU_BIAS": 4,
-             "DRELU_BGRAD": 5}
+             "DRELU_BGRAD": 5, "BIAS_RES_RMSNORM": 6, "BIAS_RES_LAYERNORM": 7}
+NORM_EPILOGUES = ("BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM")
 
 FLAG_B_TRANS = 1 << 0
 FLAG_BIAS_PER_COL = 1 << 1
@@ -97,6 +98,10 @@ def _load():
     lib.gemmepi_version.restype = i32
     lib.gemmepi_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.gemmepi_stream_read.restype = ctypes.c_int
+    lib.gemmepi_execute_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    lib.gemmepi_execute_norm.restype = ctypes.c_int
+    lib.gemmepi_norm_stats_bytes.argtypes = [i64]
+    lib.gemmepi_norm_stats_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -205,6 +210,20 @@ class Plan:
                                      _stream_handle(stream, A, B, out))
         _check(st, "gemmepi_execute")
 
+    def execute_norm(self, A: Pointer, B: Pointer, bias: Pointer, residual: Pointer,
+                     gamma: Pointer, beta: Pointer, eps: float, stats: Pointer, out: Pointer,
+                     stream=None, check: bool = True) -> None:
+        """Enqueue one GEMM + bias + residual + row-norm execution
+        (gemmepi_execute_norm); stats is an fp64 [M, 2] tensor."""
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        if check:
+            self._check_norm_tensors(A, B, bias, residual, gamma, beta, stats, out)
+        st = _load().gemmepi_execute_norm(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(residual),
+                                          _ptr(gamma), _ptr(beta), float(eps), _ptr(stats),
+                                          _ptr(out), _stream_handle(stream, A, B, out))
+        _check(st, "gemmepi_execute_norm")
+
     def info(self) -> str:
         buf = ctypes.create_string_buffer(512)
         _check(_load().gemmepi_plan_info(self._h, buf, len(buf)), "gemmepi_plan_info")
@@ -274,6 +293,39 @@ class Plan:
                 raise ValueError("aux: must be contiguous")
         if dev is not None and dev.type != "cuda":
             raise ValueError(f"operands are on {dev}; libgemmepi needs GPU (HIP) memory")
+
+
+    def _check_norm_tensors(self, A, B, bias, residual, gamma, beta, stats, out):
+        try:
+            import torch
+        except ImportError:  # pragma: no cover
+            return
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[self.dtype]
+        M, N, K = self.M, self.N, self.K
+        devs = set()
+        for t, name, dtype, numel in ((A, "A", tdt, M * K), (B, "B", tdt, N * K),
+                                      (out, "out", tdt, M * N), (bias, "bias", tdt, N),
+                                      (residual, "residual", tdt, M * N), (gamma, "gamma", tdt, N),
+                                      (beta, "beta", tdt, N), (stats, "stats", torch.float64, 2 * M)):
+            if t is None or isinstance(t, int):
+                continue
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name}: expected a torch.Tensor or an int pointer")
+            if t.dtype != dtype:
+                raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name}: must be contiguous")
+            if t.numel() != numel:
+                raise ValueError(f"{name}: {t.numel()} elements, expected {numel}")
+            devs.add(t.device)
+        if len(devs) > 1:
+            raise ValueError(f"operands on several devices: {devs}")
+        if devs and next(iter(devs)).type != "cuda":
+            raise ValueError("operands are not on the GPU; libgemmepi needs GPU (HIP) memory")
+
+
+def norm_stats_bytes(M: int) -> int:
+    return int(_load().gemmepi_norm_stats_bytes(M))
 
 
 def plan(M: int, N: int, K: int, dtype: str = "f16", epilogue: str = "BIAS", flags: int = 0,

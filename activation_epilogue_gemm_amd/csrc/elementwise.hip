@@ -7,8 +7,10 @@
 // to stream at HBM speed (128-bit accesses, grid-stride loops) so that the
 // measured fusion gain is against a competent baseline.
 //
-// Also the fp32 zero-fill used before the bias-gradient reduction (a kernel,
-// not hipMemsetAsync, so that a captured stream replays it correctly).
+// Also the fp32 zero-fill used before the bias-gradient reduction and the
+// row-statistics accumulation (a kernel, not hipMemsetAsync, so that a
+// captured stream replays it correctly), and the row norm that finishes
+// the structurally fused GEMM + residual + norm operator.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -243,6 +245,117 @@ __global__ void __launch_bounds__(512) stream_read_kernel(const u32x4* __restric
   if (acc == 0x9E3779B9u) sink[blockIdx.x & 1023] = acc;
 }
 
+
+// out = round(out + residual), both [M, ldo]; the unfused path's residual
+// connection.
+template <typename T>
+__global__ void residual_add_kernel(T* out, const T* res, int M, int N, int ldo, int vec) {
+  const int cpr = vec ? N / 8 : N;
+  const int64_t total = (int64_t)M * cpr;
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = c / cpr;
+    const int j = (int)(c - m * cpr);
+    if (vec) {
+      const int64_t at = m * ldo + j * 8;
+      float f[8], r[8];
+      unpack8<T>(*(const u32x4*)(out + at), f);
+      unpack8<T>(*(const u32x4*)(res + at), r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] += r[e];
+      *(u32x4*)(out + at) = pack8<T>(f);
+    } else {
+      const int64_t at = m * ldo + j;
+      out[at] = from_f32<T>(to_f32(out[at]) + to_f32(res[at]));
+    }
+  }
+}
+
+// Sum of a double over the 256 threads of the block; every thread gets it.
+__device__ __forceinline__ double block_sum256(double v, double* scratch) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[wave] = v;
+  __syncthreads();
+  return scratch[0] + scratch[1] + scratch[2] + scratch[3];
+}
+
+// Row norm in place (ops-nn MatMul fusion article, section "Level 2:
+// structural fusion"): one block per row at a time.  The row statistics
+// come from stats (fp64 sums of y and y^2 added by the GEMM epilogue) or,
+// for the unfused path, from the row itself; then
+//   out = (y - mean) * rstd * gamma (+ beta),  rstd = 1 / sqrt(var + eps)
+// with mean = 0 and var = mean(y^2) for RMSNorm.  (mean, rstd) are written
+// back to stats.
+template <typename T>
+__global__ void __launch_bounds__(256) norm_rows_kernel(T* out, const T* gamma, const T* beta,
+                                                        double* stats, int M, int N, int ldo,
+                                                        float eps, int layernorm, int from_stats,
+                                                        int vec) {
+  __shared__ double scratch[2][4];
+  const int tid = threadIdx.x;
+  for (int m = blockIdx.x; m < M; m += gridDim.x) {
+    T* row = out + (size_t)m * ldo;
+    double s1, s2;
+    if (from_stats) {
+      s1 = stats[2 * (size_t)m];
+      s2 = stats[2 * (size_t)m + 1];
+    } else {
+      double a = 0.0, b = 0.0;
+      if (vec) {
+        for (int n = tid * 8; n < N; n += 256 * 8) {
+          float f[8];
+          unpack8<T>(*(const u32x4*)(row + n), f);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            a += (double)f[e];
+            b += (double)f[e] * (double)f[e];
+          }
+        }
+      } else {
+        for (int n = tid; n < N; n += 256) {
+          const double v = (double)to_f32(row[n]);
+          a += v;
+          b += v * v;
+        }
+      }
+      s1 = block_sum256(a, scratch[0]);
+      s2 = block_sum256(b, scratch[1]);
+    }
+    const double mean = layernorm ? s1 / N : 0.0;
+    double var = s2 / N - mean * mean;
+    if (var < 0.0) var = 0.0;
+    const double rstd = 1.0 / sqrt(var + (double)eps);
+    const float fmean = (float)mean, frstd = (float)rstd;
+    if (vec) {
+      for (int n = tid * 8; n < N; n += 256 * 8) {
+        float f[8], g[8], bt[8];
+        unpack8<T>(*(const u32x4*)(row + n), f);
+        unpack8<T>(*(const u32x4*)(gamma + n), g);
+        if (layernorm && beta != nullptr) unpack8<T>(*(const u32x4*)(beta + n), bt);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          f[e] = (f[e] - fmean) * frstd * g[e];
+          if (layernorm && beta != nullptr) f[e] += bt[e];
+        }
+        *(u32x4*)(row + n) = pack8<T>(f);
+      }
+    } else {
+      for (int n = tid; n < N; n += 256) {
+        float v = (to_f32(row[n]) - fmean) * frstd * to_f32(gamma[n]);
+        if (layernorm && beta != nullptr) v += to_f32(beta[n]);
+        row[n] = from_f32<T>(v);
+      }
+    }
+    __syncthreads();  // every thread has read stats[m] and scratch
+    if (tid == 0) {
+      stats[2 * (size_t)m] = mean;
+      stats[2 * (size_t)m + 1] = rstd;
+    }
+  }
+}
 }  // namespace
 
 hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s) {
@@ -331,6 +444,38 @@ hipError_t launch_colsum(int dtype, const void* dz, float* bgrad, int M, int N, 
       hipLaunchKernelGGL(colsum_scalar_kernel<__bf16>, dim3((N + 255) / 256), dim3(256), 0, s,
                          (const __bf16*)dz, bgrad, M, N, ldo);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_add(int dtype, void* out, const void* residual, int M, int N, int ldo,
+                               hipStream_t s) {
+  const int vec = vec_ok(out, N, ldo) && ((uintptr_t)residual % 16 == 0);
+  const int64_t work = (int64_t)M * (vec ? N / 8 : N);
+  if (dtype == DT_F16)
+    hipLaunchKernelGGL(residual_add_kernel<_Float16>, dim3(grid_for(work, kThreads)),
+                       dim3(kThreads), 0, s, (_Float16*)out, (const _Float16*)residual, M, N, ldo,
+                       vec);
+  else
+    hipLaunchKernelGGL(residual_add_kernel<__bf16>, dim3(grid_for(work, kThreads)),
+                       dim3(kThreads), 0, s, (__bf16*)out, (const __bf16*)residual, M, N, ldo,
+                       vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_rows(int dtype, void* out, const void* gamma, const void* beta,
+                            double* stats, int M, int N, int ldo, float eps, int layernorm,
+                            int from_stats, hipStream_t s) {
+  const int vec = vec_ok(out, N, ldo) && ((uintptr_t)gamma % 16 == 0) &&
+                  (beta == nullptr || (uintptr_t)beta % 16 == 0);
+  const dim3 grid(M < 65536 ? M : 65536), block(256);
+  if (dtype == DT_F16)
+    hipLaunchKernelGGL(norm_rows_kernel<_Float16>, grid, block, 0, s, (_Float16*)out,
+                       (const _Float16*)gamma, (const _Float16*)beta, stats, M, N, ldo, eps,
+                       layernorm, from_stats, vec);
+  else
+    hipLaunchKernelGGL(norm_rows_kernel<__bf16>, grid, block, 0, s, (__bf16*)out,
+                       (const __bf16*)gamma, (const __bf16*)beta, stats, M, N, ldo, eps, layernorm,
+                       from_stats, vec);
   return hipGetLastError();
 }
 

@@ -223,8 +223,10 @@ struct GemmTile {
   static_assert((NS - 1) * LPS < 64, "vmcnt range");
   // epilogue: the output tile [BM][BN] and the per-wave-row column sums of
   // the bias gradient, [WM][BN] fp32, reuse the staging ring
+  // ([WN][BM][2] fp64 partial row sums for the norm epilogue)
   static constexpr int OUT_BYTES = BM * BN * 2;
-  static constexpr int EPI_BYTES = OUT_BYTES + WM * BN * 4;
+  static constexpr int RED_BYTES = WM * BN * 4 > BM * WN * 16 ? WM * BN * 4 : BM * WN * 16;
+  static constexpr int EPI_BYTES = OUT_BYTES + RED_BYTES;
   static constexpr int SMEM = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert(NT % (BN / 8) == 0 && BM % (NT / (BN / 8)) == 0, "epilogue copy split");
@@ -553,6 +555,77 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         for (int r = 0; r < 16; ++r)
           red[wm * BN + wn * WTN + fn * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3)] = cs[fn][r];
     }
+  } else if (epi == EPI_BIAS_RES_SUMS) {
+    // y = acc + bias[n] + residual[m, n].  The residual tile is first copied
+    // into the staging buffer with row-contiguous 16-byte loads (zeros
+    // outside the matrix); each lane then reads its values from there, adds
+    // them and writes the rounded y back in place.  Partial row sums of the
+    // rounded y and y^2 are kept in fp64 (the norm's variance is formed from
+    // them by subtraction).
+    constexpr int CPR = BN / 8, RPP = NT / CPR;
+    {
+      const T* res = (const T*)p.residual;
+      const int ch = tid % CPR;
+      const int n = n0 + ch * 8;
+      const bool vec_load = (p.ldo & 7) == 0;
+      for (int rl = tid / CPR; rl < BM; rl += RPP) {
+        const int m = m0 + rl;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (res != nullptr && m < M && n < N) {
+          const T* src = res + (size_t)m * p.ldo + n;
+          if (vec_load && n + 7 < N) {
+            v = *(const u32x4*)src;
+          } else {
+            const uint16_t* s16 = (const uint16_t*)src;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) v[e >> 1] |= (uint32_t)s16[e] << (16 * (e & 1));
+          }
+        }
+        *(u32x4*)(so + rl * (BN * 2) + ((ch ^ G::swz_o(rl)) << 4)) = v;
+      }
+    }
+    __syncthreads();
+    const T* bias = (const T*)p.bias;
+    double* red64 = (double*)(smem + G::OUT_BYTES);  // [WN][BM][2]
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int rl = wrow0 + fm * 32 + lrow;
+      const int m = m0 + rl;
+      double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int cl = wcol0 + fn * 32 + 4 * khalf;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c_loc = cl + 8 * g;
+          uint8_t* at = so + rl * (BN * 2) + (((c_loc >> 3) ^ G::swz_o(rl)) << 4) + (c_loc & 7) * 2;
+          const u32x2 rw = *(const u32x2*)at;
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = n0 + c_loc + e;
+            const uint16_t rb = (uint16_t)(rw[e >> 1] >> (16 * (e & 1)));
+            const float b = (bias != nullptr && c < N) ? to_f32(bias[c]) : 0.0f;
+            const float z = acc[fm][fn][4 * g + e] + b + to_f32(__builtin_bit_cast(T, rb));
+            y[e] = to_f32(from_f32<T>(z));  // the value stored
+            if (c < N && m < M) {
+              s1 += (double)y[e];
+              s2 += (double)y[e] * (double)y[e];
+            }
+          }
+          const u32x2 w = {pack2(y[0], y[1], T{}), pack2(y[2], y[3], T{})};
+          *(u32x2*)at = w;
+        }
+      }
+      // lanes l and l + 32 hold the two column halves of row rl
+      s1 += __shfl_xor(s1, 32);
+      s2 += __shfl_xor(s2, 32);
+      if (khalf == 0) {
+        red64[(wn * BM + rl) * 2] = s1;
+        red64[(wn * BM + rl) * 2 + 1] = s2;
+      }
+    }
   } else {
     const bool has_bias = epi != EPI_DEFAULT;
     const bool per_col = p.bias_per_col != 0;
@@ -624,6 +697,21 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     }
   }
 
+  if (epi == EPI_BIAS_RES_SUMS) {
+    const double* red64 = (const double*)(smem + G::OUT_BYTES);
+    for (int r = tid; r < BM; r += NT) {
+      const int m = m0 + r;
+      if (m >= M) continue;
+      double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) {
+        s1 += red64[(w * BM + r) * 2];
+        s2 += red64[(w * BM + r) * 2 + 1];
+      }
+      unsafeAtomicAdd(&p.stats[2 * (size_t)m], s1);
+      unsafeAtomicAdd(&p.stats[2 * (size_t)m + 1], s2);
+    }
+  }
   if (epi == EPI_DRELU_BGRAD) {
     for (int c = tid; c < BN; c += NT) {
       float s = 0.0f;

@@ -124,8 +124,9 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
 
 void describe(gemmepi_plan_s* p) {
   char buf[384];
-  static const char* epis[] = {"DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS",
-                               "DRELU_BGRAD"};
+  static const char* epis[] = {"DEFAULT",     "BIAS",        "RELU_BIAS",
+                               "RELU_AUX_BIAS", "GELU_BIAS", "DRELU_BGRAD",
+                               "BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM"};
   if (p->path == PATH_DECODE) {
     snprintf(buf, sizeof(buf),
              "path=decode M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x grid=%lld waves=8 "
@@ -186,6 +187,32 @@ gemmepi_status_t check_device_ptr(const void* p, const char* name) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// The shape, layout and raster fields of the tiled GEMM's arguments; the
+// epilogue fields are zero.
+GemmArgs gemm_args(const gemmepi_plan_s& p, const void* A, const void* B, void* out) {
+  GemmArgs g{};
+  const int N = (int)p.N, K = (int)p.K;
+  g.A = A;
+  g.B = B;
+  g.out = out;
+  g.M = (int)p.M;
+  g.N = N;
+  g.K = K;
+  g.lda = K;
+  g.ldb = (p.flags & GEMMEPI_FLAG_B_TRANS) ? K : N;
+  g.ldo = N;
+  g.aux_words = (N + 31) / 32;
+  g.tiles_m = p.tiles_m;
+  g.tiles_n = p.tiles_n;
+  g.group_m = p.group_m;
+  g.xcd_remap = p.xcd_remap;
+  g.sb_m = p.sb_m;
+  g.sb_n = p.sb_n;
+  g.xcd_m = p.xcd_m;
+  g.xcd_n = p.xcd_n;
+  return g;
+}
+
 gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
                            gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags,
                            int32_t tile_req) {
@@ -196,7 +223,7 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
                 (long long)M, (long long)N, (long long)K);
   if (dtype != GEMMEPI_F16 && dtype != GEMMEPI_BF16)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown dtype %d", (int)dtype);
-  if ((int)epi < GEMMEPI_EPI_DEFAULT || (int)epi > GEMMEPI_EPI_DRELU_BGRAD)
+  if ((int)epi < GEMMEPI_EPI_DEFAULT || (int)epi > GEMMEPI_EPI_BIAS_RES_LAYERNORM)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown epilogue %d", (int)epi);
   if (flags & ~kAllFlags) return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown flag bits 0x%x", flags);
   if (tile_req < -1 || tile_req >= kNumTiles)
@@ -289,6 +316,71 @@ gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, 
   return make_plan(plan, M, N, K, dtype, epi, flags, tile_id);
 }
 
+gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const void* B,
+                                      const void* bias, const void* residual,
+                                      const void* gamma, const void* beta, float eps,
+                                      void* stats, void* out, void* stream) {
+  if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute_norm: null plan");
+  const gemmepi_plan_s& p = *plan;
+  const int epi = p.epi;
+  if (epi != EPI_BIAS_RES_RMSNORM && epi != EPI_BIAS_RES_LAYERNORM)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute_norm: the plan's epilogue is not a norm");
+  const bool layernorm = epi == EPI_BIAS_RES_LAYERNORM;
+  const bool unfused = p.flags & GEMMEPI_FLAG_UNFUSED;
+  if (!layernorm) beta = nullptr;
+  if (!A || !B || !out || !gamma || !stats)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute_norm: A, B, gamma, stats and out are required");
+  if (!(eps > 0.0f) || !(eps < 3.0e38f))
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute_norm: eps must be positive and finite");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16) ||
+      (residual && !aligned(residual, 16)))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute_norm: A, B, residual and out must be 16-byte aligned");
+  if ((bias && !aligned(bias, 2)) || !aligned(gamma, 2) || (beta && !aligned(beta, 2)) ||
+      !aligned(stats, 8))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute_norm: bias, gamma, beta or stats misaligned");
+
+  gemmepi_status_t st = check_device();
+  if (st != GEMMEPI_OK) return st;
+  if (p.flags & GEMMEPI_FLAG_VALIDATE) {
+    const void* ptrs[] = {A, B, out, gamma, stats, bias, residual, beta};
+    const char* names[] = {"A", "B", "out", "gamma", "stats", "bias", "residual", "beta"};
+    for (int i = 0; i < 8; ++i)
+      if (ptrs[i] && (st = check_device_ptr(ptrs[i], names[i])) != GEMMEPI_OK) return st;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const int M = (int)p.M, N = (int)p.N;
+  hipError_t e = hipSuccess;
+  (void)hipGetLastError();
+  GemmArgs g = gemm_args(p, A, B, out);
+  if (!unfused) {
+    // the GEMM adds fp64 partial row sums into stats: zero them first
+    e = launch_fill_f32((float*)stats, (int64_t)M * 4, 0.0f, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "stats fill: %s", hipGetErrorString(e));
+    g.bias = bias;
+    g.residual = residual;
+    g.stats = (double*)stats;
+    g.epi = EPI_BIAS_RES_SUMS;
+    g.bias_per_col = 1;
+  } else {
+    g.epi = EPI_DEFAULT;
+  }
+  e = launch_gemm(p.dtype, (p.flags & GEMMEPI_FLAG_B_TRANS) != 0, p.tile, g, s);
+  if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
+  if (unfused) {
+    if (bias) e = launch_bias_add(p.dtype, out, bias, M, N, N, 1, s);
+    if (e == hipSuccess && residual) e = launch_residual_add(p.dtype, out, residual, M, N, N, s);
+    if (e != hipSuccess)
+      return fail(GEMMEPI_ERR_HIP, "unfused elementwise kernel: %s", hipGetErrorString(e));
+  }
+  e = launch_norm_rows(p.dtype, out, gamma, beta, (double*)stats, M, N, N, eps, layernorm ? 1 : 0,
+                       unfused ? 0 : 1, s);
+  if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "norm kernel: %s", hipGetErrorString(e));
+  return GEMMEPI_OK;
+}
+
+size_t gemmepi_norm_stats_bytes(int64_t M) { return M < 1 ? 0 : (size_t)M * 16; }
+
 gemmepi_status_t gemmepi_plan_destroy(gemmepi_plan_t plan) {
   if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "plan_destroy: null plan");
   std::lock_guard<std::mutex> lock(g_mu);
@@ -374,6 +466,8 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
   const bool needs_bias = epi != EPI_DEFAULT;  // DRELU_BGRAD: bgrad output
   const bool needs_aux = epi == EPI_RELU_AUX_BIAS || epi == EPI_DRELU_BGRAD;
 
+  if (epi == EPI_BIAS_RES_RMSNORM || epi == EPI_BIAS_RES_LAYERNORM)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: norm epilogues run through execute_norm");
   if (!A || !B || !out) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: A, B and out are required");
   if (needs_bias && !bias)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs the bias pointer%s",
@@ -426,31 +520,13 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
     e = launch_decode(p.dtype, d, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "decode kernel: %s", hipGetErrorString(e));
   } else {
-    GemmArgs g;
-    g.A = A;
-    g.B = B;
+    GemmArgs g = gemm_args(p, A, B, out);
     g.bias = bias;
     g.aux = (uint32_t*)aux;
-    g.out = out;
     g.bgrad = (float*)bias;
-    g.M = M;
-    g.N = N;
-    g.K = K;
-    g.lda = K;
-    g.ldb = bt ? K : N;
-    g.ldo = N;
     g.aux_ld = aux_ld;
-    g.aux_words = (N + 31) / 32;
     g.epi = core_epi;
     g.bias_per_col = per_col ? 1 : 0;
-    g.tiles_m = p.tiles_m;
-    g.tiles_n = p.tiles_n;
-    g.group_m = p.group_m;
-    g.xcd_remap = p.xcd_remap;
-    g.sb_m = p.sb_m;
-    g.sb_n = p.sb_n;
-    g.xcd_m = p.xcd_m;
-    g.xcd_n = p.xcd_n;
     e = launch_gemm(p.dtype, bt, p.tile, g, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
   }

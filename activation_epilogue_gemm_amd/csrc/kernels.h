@@ -14,7 +14,12 @@ enum Epi : int {
   EPI_RELU_BIAS = 2,
   EPI_RELU_AUX_BIAS = 3,
   EPI_GELU_BIAS = 4,
-  EPI_DRELU_BGRAD = 5
+  EPI_DRELU_BGRAD = 5,
+  EPI_BIAS_RES_RMSNORM = 6,
+  EPI_BIAS_RES_LAYERNORM = 7,
+  // GEMM-kernel epilogue of both norms: y = acc + bias + residual rounded
+  // to out, fp64 partial row sums of y and y^2 added into stats
+  EPI_BIAS_RES_SUMS = 8
 };
 
 enum DType : int { DT_F16 = 0, DT_BF16 = 1 };
@@ -27,6 +32,8 @@ struct GemmArgs {
   uint32_t* aux;     // packed mask [M, aux_ld] (out for RELU_AUX, in for DRELU)
   void* out;         // [M, ldo]
   float* bgrad;      // [N] fp32, pre-zeroed (DRELU_BGRAD)
+  const void* residual;  // [M, ldo] in the output dtype or null (BIAS_RES_SUMS)
+  double* stats;     // [M][2] fp64 row sums of y, y^2, pre-zeroed (BIAS_RES_SUMS)
   int M, N, K;
   int lda, ldb, ldo;
   int aux_ld;        // words per mask row
@@ -80,6 +87,14 @@ hipError_t launch_mask_apply(int dtype, void* out, const uint32_t* aux, int M, i
 hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_colsum(int dtype, const void* dz, float* bgrad, int M, int N, int ldo,
                          hipStream_t s);
+// out += residual (both [M, ldo]), rounded to the dtype
+hipError_t launch_residual_add(int dtype, void* out, const void* residual, int M, int N, int ldo,
+                               hipStream_t s);
+// Row norm of out in place: statistics from stats (fp64 sums of y and y^2,
+// from_stats = 1) or from the row itself; writes (mean, rstd) to stats.
+hipError_t launch_norm_rows(int dtype, void* out, const void* gamma, const void* beta,
+                            double* stats, int M, int N, int ldo, float eps, int layernorm,
+                            int from_stats, hipStream_t s);
 
 // per-dtype launcher tables filled by each instantiation file
 using GemmLauncher = hipError_t (*)(const GemmArgs&, hipStream_t);

@@ -118,10 +118,54 @@ class Workload:
         p.execute(A, B, self.bias, self.aux, out, check=False)
 
 
+class NormWorkload:
+    """Device buffers and plans of the GEMM + bias + residual + norm operator
+    (structural fusion); same interface as Workload."""
+
+    def __init__(self, name, case):
+        import torch
+        import activation_epilogue_gemm_amd as ge
+        self.name = name
+        c = self.case = case
+        up = lambda x: None if x is None else upload_bits(x, c.dtype, "cuda")  # noqa: E731
+        self.A, self.B = up(c.A), up(c.B)
+        self.bias, self.res, self.gamma, self.beta = up(c.bias), up(c.residual), up(c.gamma), up(c.beta)
+        self.out = torch.empty(c.M, c.N, dtype=torch_dtype(c.dtype), device="cuda")
+        self.stats = torch.empty(c.M, 2, dtype=torch.float64, device="cuda")
+        f = ge.FLAG_B_TRANS if c.b_trans else 0
+        epi = "BIAS_RES_" + c.norm
+        self.fused = ge.plan(c.M, c.N, c.K, c.dtype, epi, f)
+        self.unfused = ge.plan(c.M, c.N, c.K, c.dtype, epi, f | ge.FLAG_UNFUSED)
+        self.flops = 2.0 * c.M * c.N * c.K
+        # operands, residual, gamma/beta/bias, output and stats moved once
+        self.bytes = 2 * (c.M * c.K + c.N * c.K + 2 * c.M * c.N + 3 * c.N) + 16 * c.M
+        self.rotation = None
+
+    def run(self, unfused=False, i=0):
+        p = self.unfused if unfused else self.fused
+        p.execute_norm(self.A, self.B, self.bias, self.res, self.gamma, self.beta, self.case.eps,
+                       self.stats, self.out, check=False)
+
+
+def build_extras(only):
+    """Workloads of the 'next' rows, timed and reported beside the suite but
+    not part of its step: GEMM + bias + residual + LayerNorm / RMSNorm at the
+    2048-token FFN down-projection shape."""
+    import workloads as wl
+    sel = set(only.split(",")) if only else {"c5"}
+    extras = []
+    if "c5" in sel:
+        for norm in ("LAYERNORM", "RMSNORM"):
+            extras.append(NormWorkload(f"c5_ffn_down_res_{norm.lower()}",
+                                       wl.config5_ffn_down_norm(norm)))
+    return extras
+
+
 def build_suite(only):
     import torch
     import workloads as wl
     sel = set(only.split(",")) if only else {"c0", "c1", "c2", "c3", "c4"}
+    sel &= {"c0", "c1", "c2", "c3", "c4"}
     suite = []
     t0 = time.time()
     if "c0" in sel:
@@ -293,7 +337,10 @@ def main():
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs {props.multi_processor_count}")
 
     suite = build_suite(args.only)
-    for w in suite:
+    extras = build_extras(args.only)
+    if not suite:  # --only selected extras alone: they form the step
+        suite, extras = extras, []
+    for w in suite + extras:
         log(f"{w.name}: {w.fused.info()}")
 
     def step(i):
@@ -321,7 +368,7 @@ def main():
 
     # per-workload fused / unfused timing
     per = {}
-    for w in suite:
+    for w in suite + extras:
         reps = args.reps
         if not reps:
             t = time_region(lambda i: w.run(False, i), 3, stream)
@@ -333,6 +380,8 @@ def main():
                  "tflops": round(w.flops / f_ms / 1e9, 2),
                  "frac_mfma_peak": round(w.flops / f_ms / 1e9 / PEAK_TFLOPS, 4),
                  "plan": w.fused.info()}
+        if w in extras:
+            entry.update({"in_step": False, "gbs_algorithmic": round(w.bytes / f_ms / 1e6, 1)})
         if w.name.startswith("c1_"):
             gbs = w.bytes / f_ms / 1e6
             # the practical floor: a plain 128-bit read of the same weight bytes,

@@ -73,7 +73,13 @@ typedef enum {
   GEMMEPI_EPI_RELU_BIAS = 2,     /* out = z > 0 ? z : 0                        */
   GEMMEPI_EPI_RELU_AUX_BIAS = 3, /* RELU_BIAS, plus aux mask bit = (z > 0)    */
   GEMMEPI_EPI_GELU_BIAS = 4,     /* out = 0.5 z (1 + erf(z / sqrt 2))          */
-  GEMMEPI_EPI_DRELU_BGRAD = 5    /* out = mask ? acc : 0; bgrad[n] = sum_m out */
+  GEMMEPI_EPI_DRELU_BGRAD = 5,   /* out = mask ? acc : 0; bgrad[n] = sum_m out */
+  /* Structural fusion (ops-nn MatMul fusion article, section "Level 2:
+   * structural fusion"): y = acc + bias + residual, then a norm over each
+   * row of y (all N columns).  Executed with gemmepi_execute_norm only. */
+  GEMMEPI_EPI_BIAS_RES_RMSNORM = 6,   /* out = y / sqrt(mean(y^2) + eps) * gamma      */
+  GEMMEPI_EPI_BIAS_RES_LAYERNORM = 7  /* out = (y - mean) / sqrt(var + eps) * gamma
+                                         + beta; var biased (1/N)                  */
 } gemmepi_epilogue_t;
 
 enum {
@@ -102,7 +108,8 @@ typedef struct gemmepi_plan_s* gemmepi_plan_t;
 /*
  * Plan one GEMM shape.  Pure host work, no HIP call: validates the
  * arguments, picks the kernel (tiled MFMA GEMM, or the thin-M decode kernel
- * for M <= 16 with B_TRANS) and its tile configuration from the shape, and
+ * for M <= 16 with B_TRANS, never for the norm epilogues) and its tile
+ * configuration from the shape, and
  * returns a handle from a process-wide cache keyed on all arguments
  * (planning the same key again returns the same handle with its reference
  * count raised).
@@ -158,6 +165,49 @@ gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, 
  */
 gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
                                  void* aux, void* out, void* stream);
+/* (A plan with a norm epilogue is rejected by gemmepi_execute with
+ * INVALID_VALUE; it runs through gemmepi_execute_norm below.) */
+
+/*
+ * Enqueue one execution of a plan made with GEMMEPI_EPI_BIAS_RES_RMSNORM or
+ * GEMMEPI_EPI_BIAS_RES_LAYERNORM (ops-nn MatMul fusion article, section
+ * "Level 2: structural fusion": MatMul + bias + residual + norm as one
+ * operator; the residual joins before the norm, eps sits inside the square
+ * root, the variance is the biased one):
+ *
+ *   y[m,:]   = A[m,:] . B + bias[:] + residual[m,:]
+ *   out[m,:] = (y[m,:] - mean_m) * rstd_m * gamma[:] (+ beta[:])
+ *   LAYERNORM: mean_m = mean(y[m,:]), rstd_m = 1 / sqrt(var(y[m,:]) + eps)
+ *   RMSNORM:   mean_m = 0,            rstd_m = 1 / sqrt(mean(y[m,:]^2) + eps)
+ *
+ * The GEMM kernel writes y (rounded once to the dtype) into out and adds
+ * fp64 partial row sums of y and y^2 into stats; a second kernel then
+ * normalises each row of out in place.  With GEMMEPI_FLAG_UNFUSED the GEMM
+ * writes A.B, and separate kernels add the bias, add the residual and
+ * normalise (statistics from the row itself).
+ *
+ *   A, B      as gemmepi_execute (B [K,N], or [N,K] with B_TRANS)
+ *   bias      dtype [N] (always per column), 2-byte aligned, or NULL (none)
+ *   residual  dtype [M,N] row-major, 16-byte aligned, or NULL (none)
+ *   gamma     dtype [N], 2-byte aligned; required
+ *   beta      dtype [N], 2-byte aligned, or NULL (none); ignored by RMSNORM
+ *   eps       > 0, finite
+ *   stats     fp64 [M][2], 8-byte aligned, gemmepi_norm_stats_bytes(M)
+ *             bytes; workspace during the call, on return row m holds
+ *             (mean_m, rstd_m)
+ *   out       dtype [M,N], 16-byte aligned; overwritten (holds y between
+ *             the two kernels)
+ * Errors: INVALID_VALUE (null plan or required pointer, not a norm plan,
+ * eps not positive and finite), MISALIGNED, DEVICE (VALIDATE), HIP.
+ */
+gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const void* B,
+                                      const void* bias, const void* residual,
+                                      const void* gamma, const void* beta, float eps,
+                                      void* stats, void* out, void* stream);
+
+/* Bytes of the stats buffer of gemmepi_execute_norm for M rows (16 M);
+ * 0 for M < 1. */
+size_t gemmepi_norm_stats_bytes(int64_t M);
 
 /* Drop one reference; the plan is freed when the last reference goes.
  * Errors: INVALID_VALUE for NULL or a handle that is not live. */

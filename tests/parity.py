@@ -189,3 +189,64 @@ def check_bgrad(case, got: np.ndarray, ref, label: str = ""):
         raise AssertionError(f"{label} {case.name}: bgrad {int(bad.sum())} out of tolerance; "
                              f"{[(int(j), float(got[j]), float(ref.bgrad[j])) for j in i]}")
     return float((err / tol).max())
+
+
+# ---------------------------------------------------------------- GEMM + residual + norm
+UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def run_norm(c, flags: int = 0, tile: int = -1, eps=None):
+    """Upload a NormCase, execute it through gemmepi_execute_norm and return
+    (out bits [M, N], stats fp64 [M, 2])."""
+    import torch
+    f = flags | (ge.FLAG_B_TRANS if c.b_trans else 0)
+    up = lambda x: None if x is None else upload_bits(x, c.dtype)  # noqa: E731
+    A, B, bias, res, gamma, beta = (up(c.A), up(c.B), up(c.bias), up(c.residual), up(c.gamma),
+                                    up(c.beta))
+    out = torch.full((c.M, c.N), float("nan"), dtype=torch_dtype(c.dtype), device="cuda")
+    stats = torch.full((c.M, 2), 1234.5, dtype=torch.float64, device="cuda")
+    epi = "BIAS_RES_" + c.norm
+    with ge.plan(c.M, c.N, c.K, c.dtype, epi, f, tile=tile) as p:
+        p.execute_norm(A, B, bias, res, gamma, beta, c.eps if eps is None else eps, stats, out)
+        torch.cuda.synchronize()
+    return download_bits(out), stats.cpu().numpy()
+
+
+def norm_tolerance(c, ref, rows):
+    """Per-element bound derived from the arithmetic of
+    out = (y - mean) rstd gamma + beta: y carries the GEMM's accumulation
+    error tau = 2e-3 sqrt(K) max|A| max|B| (the bound used for every GEMM
+    here) plus two storage roundings, Delta_m = tau + 2 u max_n |y_mn|; that
+    moves the mean by at most Delta_m and rstd by a relative Delta_m rstd, so
+    |d out_mn| <= |gamma_n| rstd_m Delta_m (2 + rstd_m |y_mn - mean_m|), plus
+    1e-2 |out| for the final rounding and fp32 arithmetic and 2^-7 |beta|."""
+    u = UNIT_ROUNDOFF[c.dtype]
+    A = O.decode(c.A, c.dtype)
+    B = O.decode(c.B, c.dtype)
+    tau = 2e-3 * np.sqrt(c.K) * np.abs(A).max() * np.abs(B).max()
+    y = ref.y
+    delta = tau + 2 * u * np.abs(y).max(axis=1)                     # [R]
+    g = np.abs(O.decode(c.gamma, c.dtype))[None, :]
+    r = ref.rstd[:, None]
+    tol = 1e-2 * np.abs(ref.out64) + g * r * delta[:, None] * (2 + r * np.abs(y - ref.mean[:, None]))
+    if c.beta is not None and c.norm == "LAYERNORM":
+        tol = tol + 2.0 ** -7 * np.abs(O.decode(c.beta, c.dtype))[None, :]
+    return tol, delta
+
+
+def check_norm(c, out_bits, stats, ref, rows, label=""):
+    got = O.decode(out_bits[rows], c.dtype)
+    tol, delta = norm_tolerance(c, ref, rows)
+    err = np.abs(got - ref.out64)
+    bad = err > tol
+    assert not np.isnan(got).any(), f"{label} {c.name}: NaN in output"
+    assert not bad.any(), (f"{label} {c.name}: {int(bad.sum())} elements out of tolerance, worst "
+                           f"{float((err - tol).max()):.3g} at {np.argwhere(bad)[0].tolist()}")
+    st = stats[rows]
+    if c.norm == "LAYERNORM":
+        assert np.all(np.abs(st[:, 0] - ref.mean) <= delta + 1e-9 * np.abs(ref.mean)), \
+            f"{label} {c.name}: row means"
+    else:
+        assert np.all(st[:, 0] == 0.0), f"{label} {c.name}: RMSNorm mean slot"
+    assert np.all(np.abs(st[:, 1] - ref.rstd) <= ref.rstd * (2 * delta * ref.rstd + 1e-9)), \
+        f"{label} {c.name}: rstd"

@@ -24,7 +24,8 @@ def test_header_declares_the_api():
     for n in ("gemmepi_plan", "gemmepi_plan_tiled", "gemmepi_execute", "gemmepi_plan_destroy",
               "gemmepi_plan_info", "gemmepi_aux_ld_words", "gemmepi_aux_bytes",
               "gemmepi_status_string", "gemmepi_last_error", "gemmepi_num_tiles",
-              "gemmepi_tile_name", "gemmepi_version", "gemmepi_stream_read"):
+              "gemmepi_tile_name", "gemmepi_version", "gemmepi_stream_read",
+              "gemmepi_execute_norm", "gemmepi_norm_stats_bytes"):
         assert n in names
 
 
@@ -50,7 +51,8 @@ def test_plan_validation():
     assert _plan_status(64, -1, 64) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 1 << 31) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, dtype=2) == ge.ERR_INVALID_VALUE
-    assert _plan_status(64, 64, 64, epi=6) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, epi=8) == ge.ERR_INVALID_VALUE
+    assert _plan_status(64, 64, 64, epi=6) == ge.OK and _plan_status(64, 64, 64, epi=7) == ge.OK
     assert _plan_status(64, 64, 64, epi=-1) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, flags=1 << 9) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, tile=ge.num_tiles()) == ge.ERR_INVALID_VALUE
@@ -164,3 +166,34 @@ def test_no_oracle_in_the_product_path():
             if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_norm_entry_point_validation():
+    """execute and execute_norm reject each other's plans, and execute_norm
+    checks its pointers and eps before any HIP call."""
+    lib = ge.library()
+    assert ge.norm_stats_bytes(1000) == 16000 and ge.norm_stats_bytes(0) == 0
+    with ge.plan(64, 64, 64, "f16", "BIAS_RES_LAYERNORM", ge.FLAG_B_TRANS) as p:
+        assert "path=gemm" in p.info()          # never the decode kernel
+        h = p._h
+        assert lib.gemmepi_execute(h, 4096, 4096, 4096, 4096, 4096, None) == ge.ERR_INVALID_VALUE
+        ok = dict(A=4096, B=4096, bias=4096, res=4096, gamma=4096, beta=4096, stats=4096, out=4096)
+
+        def run(eps=1e-5, **kw):
+            a = dict(ok, **kw)
+            return lib.gemmepi_execute_norm(h, a["A"], a["B"], a["bias"], a["res"], a["gamma"],
+                                            a["beta"], eps, a["stats"], a["out"], None)
+        assert run(gamma=None) == ge.ERR_INVALID_VALUE
+        assert run(stats=None) == ge.ERR_INVALID_VALUE
+        assert run(eps=0.0) == ge.ERR_INVALID_VALUE
+        assert run(eps=-1.0) == ge.ERR_INVALID_VALUE
+        assert run(eps=float("inf")) == ge.ERR_INVALID_VALUE
+        assert run(eps=float("nan")) == ge.ERR_INVALID_VALUE
+        assert run(res=4104) == ge.ERR_MISALIGNED
+        assert run(stats=4100) == ge.ERR_MISALIGNED
+        assert run(gamma=4097) == ge.ERR_MISALIGNED
+    with ge.plan(4, 64, 64, "f16", "BIAS_RES_RMSNORM", ge.FLAG_B_TRANS) as p:
+        assert "path=gemm" in p.info()          # M <= 16 still takes the tiled GEMM
+    with ge.plan(64, 64, 64, "f16", "BIAS", 0) as p:
+        assert lib.gemmepi_execute_norm(p._h, 4096, 4096, 4096, 4096, 4096, 4096, 1e-5, 4096, 4096,
+                                        None) == ge.ERR_INVALID_VALUE

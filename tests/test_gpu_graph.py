@@ -73,3 +73,49 @@ def test_graph_replays_match_eager(epi, b_trans, tile):
             if epi == "DRELU_BGRAD":
                 assert torch.equal(cap["bias"], new["bias"]), f"replay {r}: bgrad"
         del g
+
+
+@pytest.mark.parametrize("norm", ["LAYERNORM", "RMSNORM"])
+def test_graph_replays_norm_match_eager(norm):
+    """The norm operator is three launches (statistics fill, GEMM, row norm);
+    captured and replayed with new inputs it must match eager execution."""
+    import torch
+    M, N, K = 264, 320, 136
+    cases = [wl.norm_case(M, N, K, "f16", norm, True, 300 + 11 * r, kind="int") for r in range(3)]
+
+    def bufs(c):
+        up = lambda x: upload_bits(x, "f16")  # noqa: E731
+        return {"A": up(c.A), "B": up(c.B), "bias": up(c.bias), "res": up(c.residual),
+                "gamma": up(c.gamma), "beta": up(c.beta),
+                "stats": torch.zeros(M, 2, dtype=torch.float64, device="cuda"),
+                "out": torch.empty(M, N, dtype=torch.float16, device="cuda")}
+
+    def run(p, b):
+        p.execute_norm(b["A"], b["B"], b["bias"], b["res"], b["gamma"], b["beta"], 0.25,
+                       b["stats"], b["out"])
+
+    with ge.plan(M, N, K, "f16", "BIAS_RES_" + norm, ge.FLAG_B_TRANS) as p:
+        cap = bufs(cases[0])
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run(p, cap)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(p, cap)
+        for r, c in enumerate(cases):
+            new = bufs(c)
+            for k in ("A", "B", "bias", "res", "gamma", "beta"):
+                cap[k].copy_(new[k])
+            cap["stats"].fill_(99.0)              # the replay must re-zero the sums
+            cap["out"].fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            run(p, new)
+            torch.cuda.synchronize()
+            assert np.array_equal(download_bits(cap["out"]), download_bits(new["out"])), f"replay {r}: out"
+            assert torch.equal(cap["stats"], new["stats"]), f"replay {r}: stats"
+        del g

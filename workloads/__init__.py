@@ -312,3 +312,58 @@ def random_case(M: int, N: int, K: int, dtype: str, epilogue: str, b_trans: bool
         c.bias = None
         c.aux = random_mask(M, N, seed + 3)
     return c
+
+
+@dataclasses.dataclass
+class NormCase:
+    """Operands of one GEMM + bias + residual + norm call (storage bits)."""
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str
+    norm: str                        # "RMSNORM" or "LAYERNORM"
+    b_trans: bool
+    A: Optional[np.ndarray] = None
+    B: Optional[np.ndarray] = None
+    bias: Optional[np.ndarray] = None
+    residual: Optional[np.ndarray] = None
+    gamma: Optional[np.ndarray] = None
+    beta: Optional[np.ndarray] = None
+    eps: float = 1e-5
+
+
+def norm_case(M: int, N: int, K: int, dtype: str, norm: str, b_trans: bool, seed: int,
+              kind: str = "normal", with_bias: bool = True, with_residual: bool = True,
+              with_beta: bool = True) -> NormCase:
+    """Seeded operands for the structural-fusion operator.  The residual has
+    a per-row offset (residual streams are not zero-mean), so the LayerNorm
+    mean matters.  kind="int": integer operands in {-3..3} (exact sums)."""
+    c = NormCase(f"norm_{M}x{N}x{K}_{dtype}_{norm}_{int(b_trans)}_{kind}", M, N, K, dtype, norm,
+                 b_trans)
+    if kind == "int":
+        c.A = small_ints((M, K), seed, dtype)
+        c.B = small_ints((N, K) if b_trans else (K, N), seed + 1, dtype)
+        c.bias = small_ints((N,), seed + 2, dtype) if with_bias else None
+        c.residual = small_ints((M, N), seed + 3, dtype) if with_residual else None
+        c.gamma = small_ints((N,), seed + 4, dtype)
+        c.beta = small_ints((N,), seed + 5, dtype) if with_beta else None
+        c.eps = 0.25
+        return c
+    c.A = normal((M, K), seed, 1.0, dtype)
+    c.B = normal((N, K) if b_trans else (K, N), seed + 1, 1.0 / np.sqrt(K), dtype)
+    c.bias = normal((N,), seed + 2, 0.5, dtype) if with_bias else None
+    if with_residual:
+        offs = _draw((M, 1), seed + 6, "normal", 2.0)
+        c.residual = to_bits(_draw((M, N), seed + 3, "normal", 1.0) + offs, dtype)
+    c.gamma = to_bits(1.0 + _draw((N,), seed + 4, "normal", 0.2), dtype)
+    c.beta = normal((N,), seed + 5, 0.2, dtype) if with_beta else None
+    return c
+
+
+def config5_ffn_down_norm(norm: str, dtype: str = F16) -> NormCase:
+    """The FFN down-projection of the 2048-token FFN (W2 [4096, 11008], x.W^T)
+    followed by bias + residual + norm over the 4096-wide hidden dimension:
+    the 'MatMul + residual + LayerNorm/RMSNorm' operator of the ops-nn
+    article's structural fusion, at the same shape as the FFN workloads."""
+    return norm_case(2048, 4096, 11008, dtype, norm, True, 5000 + (norm == "LAYERNORM"))

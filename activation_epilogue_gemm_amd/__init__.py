@@ -100,6 +100,8 @@ def _load():
     lib.gemmepi_stream_read.restype = ctypes.c_int
     lib.gemmepi_execute_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.gemmepi_execute_norm.restype = ctypes.c_int
+    lib.gemmepi_autotune.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(ctypes.c_float), vp]
+    lib.gemmepi_autotune.restype = ctypes.c_int
     lib.gemmepi_norm_stats_bytes.argtypes = [i64]
     lib.gemmepi_norm_stats_bytes.restype = ctypes.c_size_t
     _lib = lib
@@ -223,6 +225,21 @@ class Plan:
                                           _ptr(gamma), _ptr(beta), float(eps), _ptr(stats),
                                           _ptr(out), _stream_handle(stream, A, B, out))
         _check(st, "gemmepi_execute_norm")
+
+    def autotune(self, A: Pointer, B: Pointer, bias: Pointer = None, aux: Pointer = None,
+                 out: Pointer = None, reps: int = 5, stream=None, check: bool = True) -> dict:
+        """gemmepi_autotune: time every tile on these operands, switch the plan
+        to the fastest; returns {tile name: ms per execution}."""
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        if check:
+            self._check_tensors(A, B, bias, aux, out)
+        n = num_tiles()
+        times = (ctypes.c_float * n)()
+        st = _load().gemmepi_autotune(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(aux), _ptr(out),
+                                      int(reps), times, _stream_handle(stream, A, B, out))
+        _check(st, "gemmepi_autotune")
+        return {tile_name(t): float(times[t]) for t in range(n)}
 
     def info(self) -> str:
         buf = ctypes.create_string_buffer(512)

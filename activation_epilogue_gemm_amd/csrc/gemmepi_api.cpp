@@ -63,6 +63,7 @@ struct gemmepi_plan_s {
   int tile;
   int tiles_m, tiles_n, group_m, xcd_remap;
   int sb_m, sb_n, xcd_m, xcd_n;
+  int tuned;  // tile taken from a measured autotune result
   int k_per_wave;
   int refs;
   std::string info;
@@ -78,6 +79,64 @@ std::map<Key, gemmepi_plan_s*>& cache() {
   return c;
 }
 thread_local std::string g_err;
+
+// Measured tile choices (gemmepi_autotune), keyed by shape, dtype, epilogue
+// and flags.  With GEMMEPI_TUNE_CACHE=<path> they persist in a text file,
+// one "gemmepi-tune-v1 M N K dtype epi flags tile" line per key, read once
+// by the first plan() (host file I/O only) and rewritten by autotune.
+using TuneKey = std::tuple<int64_t, int64_t, int64_t, int, int, uint32_t>;
+std::map<TuneKey, int>& tuned() {
+  static std::map<TuneKey, int> t;
+  return t;
+}
+bool g_tune_loaded = false;
+
+const char* tune_cache_path() {
+  const char* s = getenv("GEMMEPI_TUNE_CACHE");
+  return (s && s[0]) ? s : nullptr;
+}
+
+// Caller holds g_mu.
+void load_tune_cache() {
+  if (g_tune_loaded) return;
+  g_tune_loaded = true;
+  const char* path = tune_cache_path();
+  if (!path) return;
+  FILE* f = fopen(path, "r");
+  if (!f) return;
+  char line[256];
+  while (fgets(line, sizeof line, f)) {
+    long long M, N, K;
+    int dtype, epi, tile;
+    unsigned flags;
+    char tag[32];
+    if (sscanf(line, "%31s %lld %lld %lld %d %d %u %d", tag, &M, &N, &K, &dtype, &epi, &flags,
+               &tile) != 8)
+      continue;
+    if (strcmp(tag, "gemmepi-tune-v1") != 0 || tile < 0 || tile >= kNumTiles || M < 1 || N < 1 ||
+        K < 1)
+      continue;
+    tuned()[TuneKey{M, N, K, dtype, epi, flags}] = tile;
+  }
+  fclose(f);
+}
+
+// Caller holds g_mu.  Rewrites the whole file (write to <path>.tmp, rename).
+bool save_tune_cache() {
+  const char* path = tune_cache_path();
+  if (!path) return true;
+  std::string tmp = std::string(path) + ".tmp";
+  FILE* f = fopen(tmp.c_str(), "w");
+  if (!f) return false;
+  for (auto& kv : tuned()) {
+    const TuneKey& k = kv.first;
+    fprintf(f, "gemmepi-tune-v1 %lld %lld %lld %d %d %u %d\n", (long long)std::get<0>(k),
+            (long long)std::get<1>(k), (long long)std::get<2>(k), std::get<3>(k), std::get<4>(k),
+            std::get<5>(k), kv.second);
+  }
+  const bool ok = fclose(f) == 0;
+  return ok && rename(tmp.c_str(), path) == 0;
+}
 
 gemmepi_status_t fail(gemmepi_status_t s, const char* fmt, ...) {
   char buf[512];
@@ -138,11 +197,11 @@ void describe(gemmepi_plan_s* p) {
     const TileCfg& c = kTiles[p->tile];
     snprintf(buf, sizeof(buf),
              "path=gemm M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x tile=%s tiles=%dx%d "
-             "raster=%s%s",
+             "raster=%s%s%s",
              (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
              epis[p->epi], p->flags, c.name, p->tiles_m, p->tiles_n,
              p->sb_m ? "chip16x16/xcd4x8" : (p->xcd_remap ? "xcd_remap,group8" : "group8"),
-             (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
+             p->tuned ? " tuned" : "", (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
   }
   p->info = buf;
 }
@@ -213,6 +272,30 @@ GemmArgs gemm_args(const gemmepi_plan_s& p, const void* A, const void* B, void* 
   return g;
 }
 
+// Tile, grid shape and raster of a tiled-GEMM plan.
+void set_tile(gemmepi_plan_s* p, int tile) {
+  const int64_t M = p->M, N = p->N;
+  p->path = PATH_GEMM;
+  p->tile = tile;
+  const TileCfg& c = kTiles[tile];
+  p->tiles_m = (int)((M + c.bm - 1) / c.bm);
+  p->tiles_n = (int)((N + c.bn - 1) / c.bn);
+  p->group_m = p->tiles_m < 8 ? p->tiles_m : 8;
+  const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
+  p->xcd_remap = (tiles % 8 == 0 && tiles >= 64) ? 1 : 0;
+  // chip-block raster when one round of 16 x 16 tiles (one per CU) divides
+  // the grid; XCDs take 4 x 8 sub-blocks (4 A panels, 8 B panels each)
+  p->sb_m = p->sb_n = p->xcd_m = p->xcd_n = 0;
+  const char* rast = getenv("GEMMEPI_RASTER");
+  const bool chip_ok = kTileOcc[tile] == 1 && p->tiles_m % 16 == 0 && p->tiles_n % 16 == 0;
+  if (chip_ok && !(rast && rast[0] == '0')) {
+    p->sb_m = 16;
+    p->sb_n = 16;
+    p->xcd_m = 4;
+    p->xcd_n = 2;
+  }
+}
+
 gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
                            gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags,
                            int32_t tile_req) {
@@ -268,25 +351,18 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
     const int64_t per = (K + 8 * 32 - 1) / (8 * 32) * 32;  // 8 waves, 32-wide steps
     p->k_per_wave = (int)per;
   } else {
-    p->path = PATH_GEMM;
-    p->tile = tile_req >= 0 ? tile_req : choose_tile(M, N, K);
-    const TileCfg& c = kTiles[p->tile];
-    p->tiles_m = (int)((M + c.bm - 1) / c.bm);
-    p->tiles_n = (int)((N + c.bn - 1) / c.bn);
-    p->group_m = p->tiles_m < 8 ? p->tiles_m : 8;
-    const int64_t tiles = (int64_t)p->tiles_m * p->tiles_n;
-    p->xcd_remap = (tiles % 8 == 0 && tiles >= 64) ? 1 : 0;
-    // chip-block raster when one round of 16 x 16 tiles (one per CU) divides
-    // the grid; XCDs take 4 x 8 sub-blocks (4 A panels, 8 B panels each)
-    p->sb_m = p->sb_n = p->xcd_m = p->xcd_n = 0;
-    const char* rast = getenv("GEMMEPI_RASTER");
-    const bool chip_ok = kTileOcc[p->tile] == 1 && p->tiles_m % 16 == 0 && p->tiles_n % 16 == 0;
-    if (chip_ok && !(rast && rast[0] == '0')) {
-      p->sb_m = 16;
-      p->sb_n = 16;
-      p->xcd_m = 4;
-      p->xcd_n = 2;
+    int tile = tile_req;
+    if (tile < 0) {
+      load_tune_cache();
+      auto t = tuned().find(TuneKey{M, N, K, (int)dtype, (int)epi, flags});
+      if (t != tuned().end()) {
+        tile = t->second;
+        p->tuned = 1;
+      } else {
+        tile = choose_tile(M, N, K);
+      }
     }
+    set_tile(p, tile);
   }
   describe(p);
   if (log_enabled()) fprintf(stderr, "[gemmepi] plan %s\n", p->info.c_str());
@@ -299,6 +375,100 @@ bool plan_live(gemmepi_plan_t plan) {
   for (auto& kv : cache())
     if (kv.second == plan) return true;
   return false;
+}
+
+gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void* B, void* bias,
+                              void* aux, void* out, void* stream) {
+  const int epi = p.epi;
+  const bool bt = p.flags & GEMMEPI_FLAG_B_TRANS;
+  const bool per_col = p.flags & GEMMEPI_FLAG_BIAS_PER_COL;
+  const bool unfused = p.flags & GEMMEPI_FLAG_UNFUSED;
+  const bool needs_bias = epi != EPI_DEFAULT;  // DRELU_BGRAD: bgrad output
+  const bool needs_aux = epi == EPI_RELU_AUX_BIAS || epi == EPI_DRELU_BGRAD;
+
+  if (epi == EPI_BIAS_RES_RMSNORM || epi == EPI_BIAS_RES_LAYERNORM)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: norm epilogues run through execute_norm");
+  if (!A || !B || !out) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: A, B and out are required");
+  if (needs_bias && !bias)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs the bias pointer%s",
+                epi == EPI_DRELU_BGRAD ? " (fp32 bgrad output)" : "");
+  if (needs_aux && !aux) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs aux");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute: A, B and out must be 16-byte aligned");
+  if (needs_bias && !aligned(bias, epi == EPI_DRELU_BGRAD ? 4 : 2))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute: bias misaligned");
+  if (needs_aux && !aligned(aux, 16))
+    return fail(GEMMEPI_ERR_MISALIGNED, "execute: aux must be 16-byte aligned");
+
+  gemmepi_status_t st = check_device();
+  if (st != GEMMEPI_OK) return st;
+  if (p.flags & GEMMEPI_FLAG_VALIDATE) {
+    if ((st = check_device_ptr(A, "A")) != GEMMEPI_OK) return st;
+    if ((st = check_device_ptr(B, "B")) != GEMMEPI_OK) return st;
+    if ((st = check_device_ptr(out, "out")) != GEMMEPI_OK) return st;
+    if (needs_bias && (st = check_device_ptr(bias, "bias")) != GEMMEPI_OK) return st;
+    if (needs_aux && (st = check_device_ptr(aux, "aux")) != GEMMEPI_OK) return st;
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  const int M = (int)p.M, N = (int)p.N, K = (int)p.K;
+  const int aux_ld = (int)gemmepi_aux_ld_words(N);
+  const int core_epi = unfused ? EPI_DEFAULT : epi;
+  hipError_t e = hipSuccess;
+  (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
+
+  if (epi == EPI_DRELU_BGRAD) {
+    e = launch_fill_f32((float*)bias, N, 0.0f, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "bgrad fill: %s", hipGetErrorString(e));
+  }
+
+  if (p.path == PATH_DECODE) {
+    DecodeArgs d;
+    d.x = A;
+    d.W = B;
+    d.bias = bias;
+    d.out = out;
+    d.M = M;
+    d.N = N;
+    d.K = K;
+    d.ldx = K;
+    d.ldw = K;
+    d.ldo = N;
+    d.k_per_wave = p.k_per_wave;
+    d.epi = core_epi;
+    d.bias_per_col = per_col ? 1 : 0;
+    e = launch_decode(p.dtype, d, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "decode kernel: %s", hipGetErrorString(e));
+  } else {
+    GemmArgs g = gemm_args(p, A, B, out);
+    g.bias = bias;
+    g.aux = (uint32_t*)aux;
+    g.bgrad = (float*)bias;
+    g.aux_ld = aux_ld;
+    g.epi = core_epi;
+    g.bias_per_col = per_col ? 1 : 0;
+    e = launch_gemm(p.dtype, bt, p.tile, g, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
+  }
+
+  if (unfused) {
+    switch (epi) {
+      case EPI_DEFAULT:
+        break;
+      case EPI_DRELU_BGRAD:
+        e = launch_mask_apply(p.dtype, out, (const uint32_t*)aux, M, N, N, aux_ld, s);
+        if (e == hipSuccess) e = launch_colsum(p.dtype, out, (float*)bias, M, N, N, s);
+        break;
+      default:
+        e = launch_bias_add(p.dtype, out, bias, M, N, N, per_col ? 1 : 0, s);
+        if (e == hipSuccess && epi != EPI_BIAS)
+          e = launch_activation(p.dtype, epi, out, (uint32_t*)aux, M, N, N, aux_ld, s);
+        break;
+    }
+    if (e != hipSuccess)
+      return fail(GEMMEPI_ERR_HIP, "unfused elementwise kernel: %s", hipGetErrorString(e));
+  }
+  return GEMMEPI_OK;
 }
 
 }  // namespace
@@ -456,98 +626,67 @@ gemmepi_status_t gemmepi_stream_read(const void* p, size_t bytes, void* sink, vo
 gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
                                  void* aux, void* out, void* stream) {
   if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: null plan");
-  // The plan is immutable after creation; callers keep it alive while they
-  // execute it, so no lock is taken on this path.
-  const gemmepi_plan_s& p = *plan;
-  const int epi = p.epi;
-  const bool bt = p.flags & GEMMEPI_FLAG_B_TRANS;
-  const bool per_col = p.flags & GEMMEPI_FLAG_BIAS_PER_COL;
-  const bool unfused = p.flags & GEMMEPI_FLAG_UNFUSED;
-  const bool needs_bias = epi != EPI_DEFAULT;  // DRELU_BGRAD: bgrad output
-  const bool needs_aux = epi == EPI_RELU_AUX_BIAS || epi == EPI_DRELU_BGRAD;
+  // The plan is immutable after creation (autotune excepted); callers keep
+  // it alive while they execute it, so no lock is taken on this path.
+  return execute_impl(*plan, A, B, bias, aux, out, stream);
+}
 
-  if (epi == EPI_BIAS_RES_RMSNORM || epi == EPI_BIAS_RES_LAYERNORM)
-    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: norm epilogues run through execute_norm");
-  if (!A || !B || !out) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: A, B and out are required");
-  if (needs_bias && !bias)
-    return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs the bias pointer%s",
-                epi == EPI_DRELU_BGRAD ? " (fp32 bgrad output)" : "");
-  if (needs_aux && !aux) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs aux");
-  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16))
-    return fail(GEMMEPI_ERR_MISALIGNED, "execute: A, B and out must be 16-byte aligned");
-  if (needs_bias && !aligned(bias, epi == EPI_DRELU_BGRAD ? 4 : 2))
-    return fail(GEMMEPI_ERR_MISALIGNED, "execute: bias misaligned");
-  if (needs_aux && !aligned(aux, 16))
-    return fail(GEMMEPI_ERR_MISALIGNED, "execute: aux must be 16-byte aligned");
-
-  gemmepi_status_t st = check_device();
-  if (st != GEMMEPI_OK) return st;
-  if (p.flags & GEMMEPI_FLAG_VALIDATE) {
-    if ((st = check_device_ptr(A, "A")) != GEMMEPI_OK) return st;
-    if ((st = check_device_ptr(B, "B")) != GEMMEPI_OK) return st;
-    if ((st = check_device_ptr(out, "out")) != GEMMEPI_OK) return st;
-    if (needs_bias && (st = check_device_ptr(bias, "bias")) != GEMMEPI_OK) return st;
-    if (needs_aux && (st = check_device_ptr(aux, "aux")) != GEMMEPI_OK) return st;
-  }
-
+gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
+                                  void* aux, void* out, int32_t reps, float* times_ms,
+                                  void* stream) {
+  if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "autotune: null plan");
+  if (reps < 1 || reps > 10000) return fail(GEMMEPI_ERR_INVALID_VALUE, "autotune: reps %d", reps);
+  gemmepi_plan_s& p = *plan;
+  if (p.path != PATH_GEMM)
+    return fail(GEMMEPI_ERR_UNSUPPORTED, "autotune: the decode kernel has no tile to tune");
+  if (p.epi == EPI_BIAS_RES_RMSNORM || p.epi == EPI_BIAS_RES_LAYERNORM)
+    return fail(GEMMEPI_ERR_UNSUPPORTED, "autotune: norm plans are not tuned");
+  if (p.tile_req >= 0)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "autotune: the plan has an explicit tile");
   hipStream_t s = (hipStream_t)stream;
-  const int M = (int)p.M, N = (int)p.N, K = (int)p.K;
-  const int aux_ld = (int)gemmepi_aux_ld_words(N);
-  const int core_epi = unfused ? EPI_DEFAULT : epi;
-  hipError_t e = hipSuccess;
-  (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
-
-  if (epi == EPI_DRELU_BGRAD) {
-    e = launch_fill_f32((float*)bias, N, 0.0f, s);
-    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "bgrad fill: %s", hipGetErrorString(e));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(GEMMEPI_ERR_HIP, "autotune: event creation failed");
   }
-
-  if (p.path == PATH_DECODE) {
-    DecodeArgs d;
-    d.x = A;
-    d.W = B;
-    d.bias = bias;
-    d.out = out;
-    d.M = M;
-    d.N = N;
-    d.K = K;
-    d.ldx = K;
-    d.ldw = K;
-    d.ldo = N;
-    d.k_per_wave = p.k_per_wave;
-    d.epi = core_epi;
-    d.bias_per_col = per_col ? 1 : 0;
-    e = launch_decode(p.dtype, d, s);
-    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "decode kernel: %s", hipGetErrorString(e));
-  } else {
-    GemmArgs g = gemm_args(p, A, B, out);
-    g.bias = bias;
-    g.aux = (uint32_t*)aux;
-    g.bgrad = (float*)bias;
-    g.aux_ld = aux_ld;
-    g.epi = core_epi;
-    g.bias_per_col = per_col ? 1 : 0;
-    e = launch_gemm(p.dtype, bt, p.tile, g, s);
-    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
-  }
-
-  if (unfused) {
-    switch (epi) {
-      case EPI_DEFAULT:
-        break;
-      case EPI_DRELU_BGRAD:
-        e = launch_mask_apply(p.dtype, out, (const uint32_t*)aux, M, N, N, aux_ld, s);
-        if (e == hipSuccess) e = launch_colsum(p.dtype, out, (float*)bias, M, N, N, s);
-        break;
-      default:
-        e = launch_bias_add(p.dtype, out, bias, M, N, N, per_col ? 1 : 0, s);
-        if (e == hipSuccess && epi != EPI_BIAS)
-          e = launch_activation(p.dtype, epi, out, (uint32_t*)aux, M, N, N, aux_ld, s);
-        break;
+  int best = -1;
+  float best_ms = 0.0f;
+  gemmepi_status_t st = GEMMEPI_OK;
+  for (int t = 0; t < kNumTiles && st == GEMMEPI_OK; ++t) {
+    gemmepi_plan_s q = p;  // same operands, another tile
+    set_tile(&q, t);
+    st = execute_impl(q, A, B, bias, aux, out, stream);  // warm-up (validates the arguments)
+    if (st != GEMMEPI_OK) break;
+    hipError_t e = hipEventRecord(e0, s);
+    for (int r = 0; r < reps && st == GEMMEPI_OK; ++r)
+      st = execute_impl(q, A, B, bias, aux, out, stream);
+    if (st != GEMMEPI_OK) break;
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+    if (e != hipSuccess) {
+      st = fail(GEMMEPI_ERR_HIP, "autotune timing: %s", hipGetErrorString(e));
+      break;
     }
-    if (e != hipSuccess)
-      return fail(GEMMEPI_ERR_HIP, "unfused elementwise kernel: %s", hipGetErrorString(e));
+    ms /= (float)reps;
+    if (times_ms) times_ms[t] = ms;
+    if (best < 0 || ms < best_ms) {
+      best = t;
+      best_ms = ms;
+    }
   }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != GEMMEPI_OK) return st;
+  std::lock_guard<std::mutex> lock(g_mu);
+  load_tune_cache();
+  tuned()[TuneKey{p.M, p.N, p.K, p.dtype, p.epi, p.flags}] = best;
+  set_tile(&p, best);
+  p.tuned = 1;
+  describe(&p);
+  if (!save_tune_cache())
+    return fail(GEMMEPI_ERR_HIP, "autotune: could not write %s", tune_cache_path());
   return GEMMEPI_OK;
 }
 

@@ -169,6 +169,31 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
  * INVALID_VALUE; it runs through gemmepi_execute_norm below.) */
 
 /*
+ * Measured tile choice for a tiled-GEMM plan: the pages' planner "tries
+ * multiple algorithms" and keeps the best ("nvmath-python cuBLASLt bias
+ * fusion guide", section "Advanced techniques and engineering practice";
+ * "Fusing bias addition ...", paragraph 5).  Executes the plan with every
+ * tile configuration on the caller's operands (one warm-up and `reps` timed
+ * runs each, HIP events on `stream`), then waits for the stream.  The plan
+ * is switched to the fastest tile in place (plan_info then says "tuned"),
+ * later gemmepi_plan calls for the same M, N, K, dtype, epilogue and flags
+ * use it, and with GEMMEPI_TUNE_CACHE=<file> the choice is written to that
+ * text file, which the first gemmepi_plan of a later process reads.
+ *
+ *   A..out   as gemmepi_execute; out, aux and bgrad are overwritten
+ *   reps     1 .. 10000
+ *   times_ms NULL, or gemmepi_num_tiles() floats receiving each tile's mean
+ *            milliseconds per execution
+ * Not thread-safe against executions of the same plan on other threads.
+ * Errors: INVALID_VALUE (null plan, reps, a plan made with an explicit
+ * tile), UNSUPPORTED (decode or norm plans), the errors of
+ * gemmepi_execute, HIP (timing, or the cache file could not be written).
+ */
+gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
+                                  void* aux, void* out, int32_t reps, float* times_ms,
+                                  void* stream);
+
+/*
  * Enqueue one execution of a plan made with GEMMEPI_EPI_BIAS_RES_RMSNORM or
  * GEMMEPI_EPI_BIAS_RES_LAYERNORM (ops-nn MatMul fusion article, section
  * "Level 2: structural fusion": MatMul + bias + residual + norm as one

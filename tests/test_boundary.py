@@ -25,7 +25,7 @@ def test_header_declares_the_api():
               "gemmepi_plan_info", "gemmepi_aux_ld_words", "gemmepi_aux_bytes",
               "gemmepi_status_string", "gemmepi_last_error", "gemmepi_num_tiles",
               "gemmepi_tile_name", "gemmepi_version", "gemmepi_stream_read",
-              "gemmepi_execute_norm", "gemmepi_norm_stats_bytes"):
+              "gemmepi_execute_norm", "gemmepi_norm_stats_bytes", "gemmepi_autotune"):
         assert n in names
 
 
@@ -197,3 +197,39 @@ def test_norm_entry_point_validation():
     with ge.plan(64, 64, 64, "f16", "BIAS", 0) as p:
         assert lib.gemmepi_execute_norm(p._h, 4096, 4096, 4096, 4096, 4096, 4096, 1e-5, 4096, 4096,
                                         None) == ge.ERR_INVALID_VALUE
+
+
+def test_autotune_validation_before_any_hip_call():
+    lib = ge.library()
+    assert lib.gemmepi_autotune(None, 4096, 4096, 4096, 4096, 4096, 3, None, None) == ge.ERR_INVALID_VALUE
+    with ge.plan(512, 512, 512, "f16", "BIAS", 0) as p:
+        assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, 4096, 4096, 0, None, None) == ge.ERR_INVALID_VALUE
+    with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", ge.FLAG_B_TRANS | ge.FLAG_BIAS_PER_COL) as p:
+        assert "path=decode" in p.info()
+        assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, 4096, 4096, 3, None, None) == ge.ERR_UNSUPPORTED
+    with ge.plan(512, 512, 512, "f16", "BIAS_RES_LAYERNORM", 0) as p:
+        assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, 4096, 4096, 3, None, None) == ge.ERR_UNSUPPORTED
+    with ge.plan(512, 512, 512, "f16", "BIAS", 0, tile=3) as p:
+        assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, 4096, 4096, 3, None, None) == ge.ERR_INVALID_VALUE
+
+
+def test_tune_cache_file_is_read_by_a_new_process(tmp_path):
+    """The first plan() of a process reads GEMMEPI_TUNE_CACHE: a valid line
+    sets the tile of its key; malformed lines and unknown tiles are ignored."""
+    import subprocess
+    import sys
+    f = tmp_path / "tune.txt"
+    f.write_text("gemmepi-tune-v1 1000 1000 1000 0 1 0 5\n"      # f16 BIAS, no flags -> tile 5
+                 "garbage line\n"
+                 "gemmepi-tune-v1 2000 2000 2000 0 1 0 99\n"     # tile out of range
+                 "gemmepi-tune-v2 3000 3000 3000 0 1 0 4\n")     # unknown version
+    code = ("import activation_epilogue_gemm_amd as ge\n"
+            "for m in (1000, 2000, 3000):\n"
+            "    with ge.plan(m, m, m, 'f16', 'BIAS', 0) as p: print(p.info())\n")
+    env = dict(os.environ, GEMMEPI_TUNE_CACHE=str(f), PYTHONPATH=ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = r.stdout.strip().splitlines()
+    assert ge.tile_name(5) in lines[0] and "tuned" in lines[0]
+    assert "tuned" not in lines[1] and "tuned" not in lines[2]

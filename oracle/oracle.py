@@ -29,6 +29,12 @@ with these epilogues (the MatmulEpilog members the pages name):
   DRELU_BGRAD    backward of ReLU+bias: dZ = mask ? acc : 0 and
                  bgrad[j] = sum_i dZ[i,j] ("nvmath-python cuBLASLt bias fusion
                  guide", section "Advanced techniques and engineering practice")
+  GELU_AUX_BIAS  as GELU_BIAS, plus the pre-activation z (rounded once to the
+                 storage dtype) kept as the auxiliary output, the GELU
+                 counterpart of RELU_AUX_BIAS's mask
+  DGELU_BGRAD    backward of GELU+bias, the GELU counterpart of DRELU_BGRAD:
+                 dZ = acc * gelu'(z) with z the stored pre-activation and
+                 gelu'(z) = Phi(z) + z phi(z); bgrad[j] = sum_i dZ[i,j]
 
 Readings where the pages are silent (each listed in the design notes):
   * accumulate in fp32 on the device, fp64 here; alpha = 1, beta = 0;
@@ -67,7 +73,8 @@ from typing import Optional
 
 import numpy as np
 
-EPILOGUES = ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "DRELU_BGRAD")
+EPILOGUES = ("DEFAULT", "BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "DRELU_BGRAD",
+             "GELU_AUX_BIAS", "DGELU_BGRAD")
 NORMS = ("RMSNORM", "LAYERNORM")
 
 
@@ -158,6 +165,15 @@ def gelu(z: np.ndarray) -> np.ndarray:
     return 0.5 * z * _erfc(-z / math.sqrt(2.0)).astype(np.float64)
 
 
+def gelu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz of z Phi(z): Phi(z) + z phi(z), phi the standard normal density
+    exp(-z^2 / 2) / sqrt(2 pi)."""
+    z = np.asarray(z, dtype=np.float64)
+    Phi = 0.5 * _erfc(-z / math.sqrt(2.0)).astype(np.float64)
+    phi = np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+    return Phi + z * phi
+
+
 def aux_ld_words(n: int) -> int:
     """Mask row pitch in uint32 words."""
     return ((n + 31) // 32 + 3) // 4 * 4
@@ -194,6 +210,7 @@ class OracleResult:
     z: np.ndarray                    # fp64 pre-activation (acc + bias, or acc) [R, N]
     y: np.ndarray                    # fp64 epilogue value before rounding [R, N]
     mask: Optional[np.ndarray] = None    # RELU_AUX_BIAS: uint32 [R, ld]
+    zaux: Optional[np.ndarray] = None    # GELU_AUX_BIAS: storage bits of z [R, N]
     bgrad: Optional[np.ndarray] = None   # DRELU_BGRAD: float32 [N]
 
 
@@ -205,8 +222,9 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
 
     A: storage bits [M, K];  B: [K, N], or [N, K] when ``b_trans``;
     bias: [M] (or [N] with ``bias_per_col``) storage bits, for the *_BIAS
-    epilogues; aux: packed input mask for DRELU_BGRAD.  ``rows`` restricts the
-    returned rows (DRELU_BGRAD still reduces bgrad over every row).
+    epilogues; aux: packed input mask for DRELU_BGRAD, storage bits of the
+    saved pre-activation [M, N] for DGELU_BGRAD.  ``rows`` restricts the
+    returned rows (the BGRAD epilogues still reduce bgrad over every row).
     """
     if epilogue not in EPILOGUES:
         raise ValueError(epilogue)
@@ -216,12 +234,12 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
         B64 = B64.T
     all_rows = np.arange(M)
     rows = all_rows if rows is None else np.asarray(rows)
-    need_all = epilogue == "DRELU_BGRAD"
+    need_all = epilogue in ("DRELU_BGRAD", "DGELU_BGRAD")
     comp_rows = all_rows if need_all else rows
 
     acc = A64[comp_rows] @ B64                         # [R, N] fp64
 
-    if epilogue in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS"):
+    if epilogue in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "GELU_AUX_BIAS"):
         b64 = decode(np.asarray(bias), dtype)
         if bias_per_col:
             z = acc + b64[None, :N]
@@ -231,6 +249,7 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
         z = acc
 
     mask_words = None
+    zaux = None
     bgrad = None
     if epilogue in ("DEFAULT", "BIAS"):
         y = z
@@ -238,8 +257,14 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
         y = np.where(z > 0, z, 0.0)
         if epilogue == "RELU_AUX_BIAS":
             mask_words = pack_mask(z > 0)
-    elif epilogue == "GELU_BIAS":
+    elif epilogue in ("GELU_BIAS", "GELU_AUX_BIAS"):
         y = gelu(z)
+        if epilogue == "GELU_AUX_BIAS":
+            zaux = encode(z, dtype)
+    elif epilogue == "DGELU_BGRAD":
+        zs = decode(np.asarray(aux).reshape(M, N), dtype)
+        y = z * gelu_grad(zs)
+        bgrad = y.sum(axis=0).astype(np.float32)
     else:  # DRELU_BGRAD
         m = unpack_mask(np.asarray(aux).reshape(M, -1), N)
         y = np.where(m, z, 0.0)
@@ -249,7 +274,7 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
     if need_all and rows is not comp_rows:
         sel = rows
         out, z, y = out[sel], z[sel], y[sel]
-    return OracleResult(rows=rows, out=out, z=z, y=y, mask=mask_words, bgrad=bgrad)
+    return OracleResult(rows=rows, out=out, z=z, y=y, mask=mask_words, bgrad=bgrad, zaux=zaux)
 
 
 def ffn_block(x, W1, b1, W2, b2, tokens: int, hidden: int, inter: int, dtype: str):

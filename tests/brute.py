@@ -77,15 +77,18 @@ def f32_round(x: float) -> float:
 def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
           mask_words: Optional[Sequence[Sequence[int]]], M: int, N: int, K: int,
           dtype: str, epilogue: str, b_trans: bool, bias_per_col: bool):
-    """Returns (out_bits[M][N], mask_bits[M][N] or None, bgrad[N] or None).
+    """Returns (out_bits[M][N], mask bits or z bits [M][N] or None, bgrad[N]
+    or None).
 
-    A, B, bias are flat sequences of storage bits (row-major)."""
+    A, B, bias are flat sequences of storage bits (row-major); mask_words is
+    the packed mask [M][words] for DRELU_BGRAD and the flat z storage bits
+    [M*N] for DGELU_BGRAD."""
     a = [[value(A[i * K + k], dtype) for k in range(K)] for i in range(M)]
     if b_trans:
         b = [[value(B[j * K + k], dtype) for j in range(N)] for k in range(K)]
     else:
         b = [[value(B[k * N + j], dtype) for j in range(N)] for k in range(K)]
-    has_bias = epilogue in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS")
+    has_bias = epilogue in ("BIAS", "RELU_BIAS", "RELU_AUX_BIAS", "GELU_BIAS", "GELU_AUX_BIAS")
     out: List[List[int]] = []
     mask: List[List[bool]] = []
     colsum_terms: List[List[float]] = [[] for _ in range(N)]
@@ -101,8 +104,14 @@ def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
             elif epilogue in ("RELU_BIAS", "RELU_AUX_BIAS"):
                 y = z if z > 0 else 0.0
                 mrow.append(z > 0)
-            elif epilogue == "GELU_BIAS":
+            elif epilogue in ("GELU_BIAS", "GELU_AUX_BIAS"):
                 y = 0.5 * z * math.erfc(-z / math.sqrt(2.0))
+                mrow.append(out_bits(z, dtype))
+            elif epilogue == "DGELU_BGRAD":
+                zs = value(mask_words[i * N + j], dtype)       # saved pre-activation bits
+                g = 0.5 * math.erfc(-zs / math.sqrt(2.0)) + zs * math.exp(-0.5 * zs * zs) / math.sqrt(2.0 * math.pi)
+                y = z * g
+                colsum_terms[j].append(y)
             elif epilogue == "DRELU_BGRAD":
                 bit = (mask_words[i][j >> 5] >> (j & 31)) & 1
                 y = z if bit else 0.0
@@ -114,9 +123,10 @@ def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
         out.append(orow)
         mask.append(mrow)
     bgrad = None
-    if epilogue == "DRELU_BGRAD":
+    if epilogue in ("DRELU_BGRAD", "DGELU_BGRAD"):
         bgrad = [f32_round(math.fsum(t)) for t in colsum_terms]
-    return out, (mask if epilogue == "RELU_AUX_BIAS" else None), bgrad
+    # RELU_AUX_BIAS: mask bits; GELU_AUX_BIAS: storage bits of z
+    return out, (mask if epilogue in ("RELU_AUX_BIAS", "GELU_AUX_BIAS") else None), bgrad
 
 
 def norm(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],

@@ -78,7 +78,12 @@ def test_brute_force_tiny(epi, dtype):
                 c = wl.random_case(M, N, K, dtype, epi, b_trans, per_col, seed)
                 r = O.gemm_epilogue(c.A, c.B, c.bias, c.aux, M, N, K, dtype, epi,
                                     b_trans, per_col)
-                mask_in = c.aux.tolist() if c.aux is not None else None
+                if c.aux is None:
+                    mask_in = None
+                elif epi == "DGELU_BGRAD":
+                    mask_in = c.aux.ravel().tolist()
+                else:
+                    mask_in = c.aux.tolist()
                 bout, bmask, bbgrad = brute.fused(
                     c.A.ravel().tolist(), c.B.ravel().tolist(),
                     None if c.bias is None else c.bias.tolist(), mask_in,
@@ -86,7 +91,9 @@ def test_brute_force_tiny(epi, dtype):
                 assert r.out.tolist() == bout, (M, N, K, b_trans, per_col)
                 if epi == "RELU_AUX_BIAS":
                     assert np.array_equal(O.unpack_mask(r.mask, N), np.array(bmask, bool))
-                if epi == "DRELU_BGRAD":
+                if epi == "GELU_AUX_BIAS":
+                    assert r.zaux.tolist() == bmask
+                if epi in ("DRELU_BGRAD", "DGELU_BGRAD"):
                     assert r.bgrad.tolist() == bbgrad
 
 
@@ -374,3 +381,46 @@ def test_norm_invariants():
     sub = O.gemm_norm(A, B, bias, res, ones, zeros, 1e-3, M, N, K, "f16", "LAYERNORM", False,
                       rows=np.array([4, 1]))
     assert np.array_equal(sub.out, both.out[[4, 1]])
+
+
+
+# ---------------------------------------------------------------- GELU backward
+def test_gelu_grad_closed_forms():
+    """gelu'(z) = Phi(z) + z phi(z): gelu'(0) = 1/2; gelu'(1) and gelu'(-1)
+    from the standard-normal table values Phi(1) (tests/golden/normal_cdf.json)
+    and phi(1) = exp(-1/2) / sqrt(2 pi); gelu'(z) + gelu'(-z) = 1 (the
+    derivative of gelu(z) - gelu(-z) = z); the far tails tend to 1 and 0."""
+    Phi1 = dict((float(k), v) for k, v in _golden("normal_cdf.json")["phi"])[1.0]
+    phi1 = 0.24197072451914337   # exp(-1/2) / sqrt(2 pi), the standard normal density at 1
+    assert O.gelu_grad(np.array([0.0]))[0] == 0.5
+    assert abs(O.gelu_grad(np.array([1.0]))[0] - (Phi1 + phi1)) < 1e-12
+    assert abs(O.gelu_grad(np.array([-1.0]))[0] - (1.0 - Phi1 - phi1)) < 1e-12
+    z = np.linspace(-9, 9, 721)
+    assert np.allclose(O.gelu_grad(z) + O.gelu_grad(-z), 1.0, rtol=0, atol=1e-15)
+    assert abs(O.gelu_grad(np.array([12.0]))[0] - 1.0) < 1e-15
+    assert 0.0 > O.gelu_grad(np.array([-6.0]))[0] > -1e-7
+
+
+def test_gelu_grad_is_the_derivative_of_gelu():
+    """Central differences of the oracle's own gelu agree with gelu_grad."""
+    z = np.linspace(-7, 7, 281)
+    h = 1e-5
+    fd = (O.gelu(z + h) - O.gelu(z - h)) / (2 * h)
+    assert np.allclose(fd, O.gelu_grad(z), rtol=0, atol=2e-9)
+
+
+def test_gelu_aux_and_dgelu_compose():
+    """GELU_AUX_BIAS keeps z = the BIAS epilogue's output bits and the same
+    out as GELU_BIAS; DGELU_BGRAD with z = 0 everywhere halves the DEFAULT
+    product (gelu'(0) = 1/2) and its bgrad is the column sum."""
+    M, N, K = 6, 20, 9
+    c = wl.random_case(M, N, K, "f16", "GELU_AUX_BIAS", True, True, 12)
+    aux = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, "f16", "GELU_AUX_BIAS", True, True)
+    gl = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, "f16", "GELU_BIAS", True, True)
+    bs = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, "f16", "BIAS", True, True)
+    assert np.array_equal(aux.out, gl.out) and np.array_equal(aux.zaux, bs.out)
+    zeros = np.zeros((M, N), dtype=np.uint16)
+    d = O.gemm_epilogue(c.A, c.B, None, zeros, M, N, K, "f16", "DGELU_BGRAD", True, False)
+    base = O.gemm_epilogue(c.A, c.B, None, None, M, N, K, "f16", "DEFAULT", True, False)
+    assert np.array_equal(d.y, 0.5 * base.y)
+    assert np.array_equal(d.bgrad, (0.5 * base.y).sum(axis=0).astype(np.float32))

@@ -311,6 +311,10 @@ def random_case(M: int, N: int, K: int, dtype: str, epilogue: str, b_trans: bool
     if epilogue == "DRELU_BGRAD":
         c.bias = None
         c.aux = random_mask(M, N, seed + 3)
+    if epilogue == "DGELU_BGRAD":
+        # the saved pre-activation z of a GELU forward, [M, N] storage bits
+        c.bias = None
+        c.aux = normal((M, N), seed + 3, 1.5, dtype)
     return c
 
 

@@ -211,7 +211,9 @@ class OracleResult:
     y: np.ndarray                    # fp64 epilogue value before rounding [R, N]
     mask: Optional[np.ndarray] = None    # RELU_AUX_BIAS: uint32 [R, ld]
     zaux: Optional[np.ndarray] = None    # GELU_AUX_BIAS: storage bits of z [R, N]
-    bgrad: Optional[np.ndarray] = None   # DRELU_BGRAD: float32 [N]
+    bgrad: Optional[np.ndarray] = None   # *_BGRAD: float32 [N]
+    bgrad_abs: Optional[np.ndarray] = None  # *_BGRAD: fp64 sum over rows of |dZ| [N]
+                                            # (the weight of a rounding-error bound)
 
 
 def gemm_epilogue(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
@@ -269,12 +271,14 @@ def gemm_epilogue(A: np.ndarray, B: np.ndarray, bias: Optional[np.ndarray],
         m = unpack_mask(np.asarray(aux).reshape(M, -1), N)
         y = np.where(m, z, 0.0)
         bgrad = y.sum(axis=0).astype(np.float32)
+    bgrad_abs = np.abs(y).sum(axis=0) if need_all else None
 
     out = encode(y, dtype)
     if need_all and rows is not comp_rows:
         sel = rows
         out, z, y = out[sel], z[sel], y[sel]
-    return OracleResult(rows=rows, out=out, z=z, y=y, mask=mask_words, bgrad=bgrad, zaux=zaux)
+    return OracleResult(rows=rows, out=out, z=z, y=y, mask=mask_words, bgrad=bgrad, zaux=zaux,
+                        bgrad_abs=bgrad_abs)
 
 
 def ffn_block(x, W1, b1, W2, b2, tokens: int, hidden: int, inter: int, dtype: str):

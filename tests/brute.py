@@ -76,13 +76,15 @@ def f32_round(x: float) -> float:
 
 def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
           mask_words: Optional[Sequence[Sequence[int]]], M: int, N: int, K: int,
-          dtype: str, epilogue: str, b_trans: bool, bias_per_col: bool):
+          dtype: str, epilogue: str, b_trans: bool, bias_per_col: bool,
+          col_abs: Optional[List[float]] = None):
     """Returns (out_bits[M][N], mask bits or z bits [M][N] or None, bgrad[N]
     or None).
 
     A, B, bias are flat sequences of storage bits (row-major); mask_words is
     the packed mask [M][words] for DRELU_BGRAD and the flat z storage bits
-    [M*N] for DGELU_BGRAD."""
+    [M*N] for DGELU_BGRAD.  For the BGRAD epilogues a list passed as
+    ``col_abs`` receives sum over rows of |dZ| per column."""
     a = [[value(A[i * K + k], dtype) for k in range(K)] for i in range(M)]
     if b_trans:
         b = [[value(B[j * K + k], dtype) for j in range(N)] for k in range(K)]
@@ -92,6 +94,7 @@ def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
     out: List[List[int]] = []
     mask: List[List[bool]] = []
     colsum_terms: List[List[float]] = [[] for _ in range(N)]
+    abs_terms: List[List[float]] = [[] for _ in range(N)]
     for i in range(M):
         orow, mrow = [], []
         for j in range(N):
@@ -119,12 +122,15 @@ def fused(A: Sequence[int], B: Sequence[int], bias: Optional[Sequence[int]],
                     colsum_terms[j].extend(terms)
             else:
                 raise ValueError(epilogue)
+            abs_terms[j].append(abs(y))
             orow.append(out_bits(y, dtype))
         out.append(orow)
         mask.append(mrow)
     bgrad = None
     if epilogue in ("DRELU_BGRAD", "DGELU_BGRAD"):
         bgrad = [f32_round(math.fsum(t)) for t in colsum_terms]
+        if col_abs is not None:
+            col_abs[:] = [math.fsum(t) for t in abs_terms]
     # RELU_AUX_BIAS: mask bits; GELU_AUX_BIAS: storage bits of z
     return out, (mask if epilogue in ("RELU_AUX_BIAS", "GELU_AUX_BIAS") else None), bgrad
 

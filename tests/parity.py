@@ -6,6 +6,14 @@ Tolerance (per element, y_ref the oracle's unrounded fp64 value):
 with the maxima over the operand tensors actually used.  The ReLU mask is
 compared bit-exactly except where |z_ref| < abs_term / 0.99 (there a result
 within the tolerance may have the other sign).  bgrad uses the same formula.
+The saved GELU pre-activation z is held to the same formula against the
+oracle's z.  For DGELU_BGRAD the accumulator's error reaches dZ = acc gelu'(z)
+scaled by |gelu'(z)| <= 1.129 (its maximum, at z = sqrt 2), so the absolute
+term of dZ and of bgrad is multiplied by that bound.  The unfused sequence
+sums dZ values that were rounded to the dtype (once for DRELU, twice for
+DGELU: the GEMM's output and the product with gelu'), so its bgrad also gets
+2 u sum_m |dZ[m, n]|, the standard bound for a sum of terms each within a
+relative 2 u of the exact one (u the dtype's unit roundoff).
 """
 from __future__ import annotations
 
@@ -34,6 +42,15 @@ def upload_words(words: np.ndarray, device="cuda"):
 def download_bits(t) -> np.ndarray:
     import torch
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+BGRAD_EPIS = ("DRELU_BGRAD", "DGELU_BGRAD")
+# GELU epilogues: the activation (or its derivative) is a transcendental
+# function, so out is compared with the tolerance even for integer inputs
+GELU_EPIS = ("GELU_BIAS", "GELU_AUX_BIAS", "DGELU_BGRAD")
+GELU_GRAD_MAX = 1.129  # max over z of |Phi(z) + z phi(z)|, attained at z = sqrt 2
+GUARD_BITS = 0x7E5A
+UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
 def flags_of(case, extra: int = 0) -> int:
@@ -66,17 +83,21 @@ class GpuRun:
         # guard bands: poison values around out / aux / bgrad
         self._out_full = torch.full((M * N + 2 * guard,), float("nan"), dtype=tdt, device=device)
         if guard:
-            self._out_full.view(torch.int16)[:guard] = 0x7E5A
-            self._out_full.view(torch.int16)[-guard:] = 0x7E5A
+            self._out_full.view(torch.int16)[:guard] = GUARD_BITS
+            self._out_full.view(torch.int16)[-guard:] = GUARD_BITS
         self.out = self._out_full[guard:guard + M * N].view(M, N)
         self.bias = None
         self.aux = None
         self._aux_full = None
+        self._zaux_full = None
         ld = ge.aux_ld_words(N)
-        if c.epilogue == "DRELU_BGRAD":
+        if c.epilogue in BGRAD_EPIS:
             self._bias_full = torch.full((N + 2 * guard,), 1234.5, dtype=torch.float32, device=device)
             self.bias = self._bias_full[guard:guard + N]
-            self.aux = upload_words(c.aux, device)
+            if c.epilogue == "DRELU_BGRAD":
+                self.aux = upload_words(c.aux, device)
+            else:
+                self.aux = upload_bits(c.aux, c.dtype, device).view(M, N)
         else:
             if c.bias is not None:
                 self.bias = upload_bits(c.bias, c.dtype, device)
@@ -84,6 +105,13 @@ class GpuRun:
                 self._aux_full = torch.full((M * ld + 2 * guard,), -0x2A2A2A2B, dtype=torch.int32,
                                             device=device)
                 self.aux = self._aux_full[guard:guard + M * ld].view(M, ld)
+            if c.epilogue == "GELU_AUX_BIAS":
+                self._zaux_full = torch.full((M * N + 2 * guard,), float("nan"), dtype=tdt,
+                                             device=device)
+                if guard:
+                    self._zaux_full.view(torch.int16)[:guard] = GUARD_BITS
+                    self._zaux_full.view(torch.int16)[-guard:] = GUARD_BITS
+                self.aux = self._zaux_full[guard:guard + M * N].view(M, N)
         self.plan = ge.plan(M, N, K, c.dtype, c.epilogue, flags_of(c, flags), tile)
         self.info = self.plan.info()
 
@@ -108,6 +136,14 @@ class GpuRun:
             a = a.index_select(0, torch.as_tensor(np.asarray(rows), device=a.device))
         return a.cpu().numpy().view(np.uint32)
 
+    def zaux_bits(self, rows=None) -> np.ndarray:
+        """GELU_AUX_BIAS: storage bits of the saved pre-activation [M, N]."""
+        if rows is None:
+            return download_bits(self.aux)
+        import torch
+        idx = torch.as_tensor(np.asarray(rows), device=self.aux.device)
+        return download_bits(self.aux.index_select(0, idx))
+
     def bgrad(self) -> np.ndarray:
         return self.bias.cpu().numpy()
 
@@ -116,12 +152,15 @@ class GpuRun:
         g = self.guard
         if not g:
             return True
-        ok = bool((self._out_full.view(torch.int16)[:g] == 0x7E5A).all()) and \
-            bool((self._out_full.view(torch.int16)[-g:] == 0x7E5A).all())
+        ok = bool((self._out_full.view(torch.int16)[:g] == GUARD_BITS).all()) and \
+            bool((self._out_full.view(torch.int16)[-g:] == GUARD_BITS).all())
+        if self._zaux_full is not None:
+            ok &= bool((self._zaux_full.view(torch.int16)[:g] == GUARD_BITS).all())
+            ok &= bool((self._zaux_full.view(torch.int16)[-g:] == GUARD_BITS).all())
         if self._aux_full is not None:
             ok &= bool((self._aux_full[:g] == -0x2A2A2A2B).all())
             ok &= bool((self._aux_full[-g:] == -0x2A2A2A2B).all())
-        if self.case.epilogue == "DRELU_BGRAD":
+        if self.case.epilogue in BGRAD_EPIS:
             ok &= bool((self._bias_full[:g] == 1234.5).all()) and bool((self._bias_full[-g:] == 1234.5).all())
         return ok
 
@@ -143,11 +182,15 @@ def abs_term(case, A_bits=None) -> float:
     return 2e-3 * np.sqrt(case.K) * amax * bmax
 
 
+def grad_scale(case) -> float:
+    return GELU_GRAD_MAX if case.epilogue == "DGELU_BGRAD" else 1.0
+
+
 def check_out(case, got_bits: np.ndarray, ref, A_bits=None, label: str = ""):
     """Element-wise tolerance check; returns the max |error| / tolerance."""
     got = O.decode(got_bits, case.dtype)
     want_y = ref.y
-    tol = 1e-2 * np.abs(want_y) + abs_term(case, A_bits)
+    tol = 1e-2 * np.abs(want_y) + grad_scale(case) * abs_term(case, A_bits)
     err = np.abs(got - want_y)
     finite = np.isfinite(got)
     bad = (~finite) | (err > tol)
@@ -180,8 +223,23 @@ def check_mask(case, got_words: np.ndarray, ref, A_bits=None, label: str = "") -
     return int((diff & excused).sum())
 
 
-def check_bgrad(case, got: np.ndarray, ref, label: str = ""):
-    tol = 1e-2 * np.abs(ref.bgrad.astype(np.float64)) + abs_term(case)
+def check_zaux(case, got_bits: np.ndarray, ref, A_bits=None, label: str = ""):
+    """GELU_AUX_BIAS: the saved z against the oracle's fp64 z."""
+    got = O.decode(got_bits, case.dtype)
+    tol = 1e-2 * np.abs(ref.z) + abs_term(case, A_bits)
+    err = np.abs(got - ref.z)
+    bad = (~np.isfinite(got)) | (err > tol)
+    if bad.any():
+        i = np.argwhere(bad)[:5]
+        raise AssertionError(f"{label} {case.name}: z aux {int(bad.sum())}/{bad.size} out of "
+                             f"tolerance, first {i.tolist()}")
+    return float((err / tol).max())
+
+
+def check_bgrad(case, got: np.ndarray, ref, label: str = "", unfused: bool = False):
+    tol = 1e-2 * np.abs(ref.bgrad.astype(np.float64)) + grad_scale(case) * abs_term(case)
+    if unfused:
+        tol = tol + 2.0 * UNIT_ROUNDOFF[case.dtype] * ref.bgrad_abs
     err = np.abs(got.astype(np.float64) - ref.bgrad.astype(np.float64))
     bad = err > tol
     if bad.any():
@@ -192,7 +250,6 @@ def check_bgrad(case, got: np.ndarray, ref, label: str = ""):
 
 
 # ---------------------------------------------------------------- GEMM + residual + norm
-UNIT_ROUNDOFF = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
 def run_norm(c, flags: int = 0, tile: int = -1, eps=None):

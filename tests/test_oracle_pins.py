@@ -84,10 +84,11 @@ def test_brute_force_tiny(epi, dtype):
                     mask_in = c.aux.ravel().tolist()
                 else:
                     mask_in = c.aux.tolist()
+                babs = []
                 bout, bmask, bbgrad = brute.fused(
                     c.A.ravel().tolist(), c.B.ravel().tolist(),
                     None if c.bias is None else c.bias.tolist(), mask_in,
-                    M, N, K, dtype, epi, b_trans, per_col)
+                    M, N, K, dtype, epi, b_trans, per_col, col_abs=babs)
                 assert r.out.tolist() == bout, (M, N, K, b_trans, per_col)
                 if epi == "RELU_AUX_BIAS":
                     assert np.array_equal(O.unpack_mask(r.mask, N), np.array(bmask, bool))
@@ -95,6 +96,7 @@ def test_brute_force_tiny(epi, dtype):
                     assert r.zaux.tolist() == bmask
                 if epi in ("DRELU_BGRAD", "DGELU_BGRAD"):
                     assert r.bgrad.tolist() == bbgrad
+                    np.testing.assert_allclose(r.bgrad_abs, babs, rtol=1e-12, atol=1e-300)
 
 
 def test_brute_force_row_subset():

@@ -37,7 +37,9 @@ ERR_NO_MEMORY = 6
 
 DTYPES = {"f16": 0, "bf16": 1}
 EPILOGUES = {"DEFAULT": 0, "BIAS": 1, "RELU_BIAS": 2, "RELU_AUX_BIAS": 3, "GELU_BIAS": 4,
-             "DRELU_BGRAD": 5, "BIAS_RES_RMSNORM": 6, "BIAS_RES_LAYERNORM": 7}
+             "DRELU_BGRAD": 5, "BIAS_RES_RMSNORM": 6, "BIAS_RES_LAYERNORM": 7,
+             "GELU_AUX_BIAS": 8, "DGELU_BGRAD": 9}
+BGRAD_EPILOGUES = ("DRELU_BGRAD", "DGELU_BGRAD")
 NORM_EPILOGUES = ("BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM")
 
 FLAG_B_TRANS = 1 << 0
@@ -296,7 +298,7 @@ class Plan:
         chk(A, "A", tdt, M * K)
         chk(B, "B", tdt, N * K)
         chk(out, "out", tdt, M * N)
-        if epi == "DRELU_BGRAD":
+        if epi in BGRAD_EPILOGUES:
             chk(bias, "bias (bgrad)", torch.float32, N)
         elif epi != "DEFAULT":
             chk(bias, "bias", tdt, N if self.flags & FLAG_BIAS_PER_COL else M)
@@ -308,6 +310,8 @@ class Plan:
                 raise ValueError(f"aux: {aux.numel()} words, expected {M * aux_ld_words(N)}")
             if not aux.is_contiguous():
                 raise ValueError("aux: must be contiguous")
+        if epi in ("GELU_AUX_BIAS", "DGELU_BGRAD"):
+            chk(aux, "aux (pre-activation z)", tdt, M * N)
         if dev is not None and dev.type != "cuda":
             raise ValueError(f"operands are on {dev}; libgemmepi needs GPU (HIP) memory")
 

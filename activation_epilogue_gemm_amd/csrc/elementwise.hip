@@ -76,9 +76,38 @@ __global__ void bias_add_kernel(T* out, const T* bias, int M, int N, int ldo, in
   }
 }
 
-// In-place ReLU or GELU, no mask.
+// In-place ReLU or GELU, no mask; with zsave the pre-activation is first
+// copied there (GELU_AUX_BIAS).
 template <typename T>
-__global__ void act_kernel(T* out, int M, int N, int ldo, int epi, int vec) {
+__global__ void act_kernel(T* out, T* zsave, int M, int N, int ldo, int epi, int vec) {
+  const int cpr = vec ? N / 8 : N;
+  const int64_t total = (int64_t)M * cpr;
+  const bool gelu = epi == EPI_GELU_BIAS || epi == EPI_GELU_AUX_BIAS;
+  for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = c / cpr;
+    const int j = (int)(c - m * cpr);
+    if (vec) {
+      u32x4* ptr = (u32x4*)(out + m * ldo + j * 8);
+      const u32x4 zw = *ptr;
+      if (zsave) *(u32x4*)(zsave + m * ldo + j * 8) = zw;
+      float f[8];
+      unpack8<T>(zw, f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = gelu ? gelu_erf(f[e]) : (f[e] > 0.0f ? f[e] : 0.0f);
+      *ptr = pack8<T>(f);
+    } else {
+      T* q = out + m * ldo + j;
+      if (zsave) zsave[m * ldo + j] = *q;
+      const float z = to_f32(*q);
+      *q = from_f32<T>(gelu ? gelu_erf(z) : (z > 0.0f ? z : 0.0f));
+    }
+  }
+}
+
+// out = round(out * gelu'(z)), z the saved pre-activation (unfused DGELU).
+template <typename T>
+__global__ void dgelu_apply_kernel(T* out, const T* z, int M, int N, int ldo, int vec) {
   const int cpr = vec ? N / 8 : N;
   const int64_t total = (int64_t)M * cpr;
   for (int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; c < total;
@@ -86,17 +115,16 @@ __global__ void act_kernel(T* out, int M, int N, int ldo, int epi, int vec) {
     const int64_t m = c / cpr;
     const int j = (int)(c - m * cpr);
     if (vec) {
-      u32x4* ptr = (u32x4*)(out + m * ldo + j * 8);
-      float f[8];
-      unpack8<T>(*ptr, f);
+      const int64_t at = m * ldo + j * 8;
+      float f[8], zz[8];
+      unpack8<T>(*(const u32x4*)(out + at), f);
+      unpack8<T>(*(const u32x4*)(z + at), zz);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        f[e] = (epi == EPI_GELU_BIAS) ? gelu_erf(f[e]) : (f[e] > 0.0f ? f[e] : 0.0f);
-      *ptr = pack8<T>(f);
+      for (int e = 0; e < 8; ++e) f[e] *= gelu_grad(zz[e]);
+      *(u32x4*)(out + at) = pack8<T>(f);
     } else {
-      T* q = out + m * ldo + j;
-      const float z = to_f32(*q);
-      *q = from_f32<T>((epi == EPI_GELU_BIAS) ? gelu_erf(z) : (z > 0.0f ? z : 0.0f));
+      const int64_t at = m * ldo + j;
+      out[at] = from_f32<T>(to_f32(out[at]) * gelu_grad(to_f32(z[at])));
     }
   }
 }
@@ -392,6 +420,7 @@ hipError_t launch_bias_add(int dtype, void* out, const void* bias, int M, int N,
 hipError_t launch_activation(int dtype, int epi, void* out, uint32_t* aux, int M, int N, int ldo,
                              int aux_ld, hipStream_t s) {
   const int vec = vec_ok(out, N, ldo);
+  void* zsave = epi == EPI_GELU_AUX_BIAS ? (void*)aux : nullptr;
   if (epi == EPI_RELU_AUX_BIAS) {
     const int aux_words = (N + 31) / 32;
     const int64_t work = (int64_t)M * aux_words * 4;
@@ -405,11 +434,24 @@ hipError_t launch_activation(int dtype, int epi, void* out, uint32_t* aux, int M
     const int64_t work = (int64_t)M * (vec ? N / 8 : N);
     if (dtype == DT_F16)
       hipLaunchKernelGGL(act_kernel<_Float16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0, s,
-                         (_Float16*)out, M, N, ldo, epi, vec);
+                         (_Float16*)out, (_Float16*)zsave, M, N, ldo, epi, vec);
     else
       hipLaunchKernelGGL(act_kernel<__bf16>, dim3(grid_for(work, kThreads)), dim3(kThreads), 0, s,
-                         (__bf16*)out, M, N, ldo, epi, vec);
+                         (__bf16*)out, (__bf16*)zsave, M, N, ldo, epi, vec);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dgelu_apply(int dtype, void* out, const void* z, int M, int N, int ldo,
+                              hipStream_t s) {
+  const int vec = vec_ok(out, N, ldo) && ((uintptr_t)z % 16 == 0);
+  const int64_t work = (int64_t)M * (vec ? N / 8 : N);
+  if (dtype == DT_F16)
+    hipLaunchKernelGGL(dgelu_apply_kernel<_Float16>, dim3(grid_for(work, kThreads)),
+                       dim3(kThreads), 0, s, (_Float16*)out, (const _Float16*)z, M, N, ldo, vec);
+  else
+    hipLaunchKernelGGL(dgelu_apply_kernel<__bf16>, dim3(grid_for(work, kThreads)),
+                       dim3(kThreads), 0, s, (__bf16*)out, (const __bf16*)z, M, N, ldo, vec);
   return hipGetLastError();
 }
 

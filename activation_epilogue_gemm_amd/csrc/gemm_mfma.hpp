@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gemm_tiles.h"
 
 #include "kernels.h"
@@ -87,6 +89,16 @@ __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint
 // Wait until at most N vector memory operations of this wave are still in
 // flight (loads complete in issue order, so every older buffer->LDS load,
 // LDS write included, has then landed).
+// f(integral_constant<int, i>) for i = 0 .. N-1: compile-time indices for
+// the accumulator array whatever the unroller decides about a large body
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
@@ -147,7 +159,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, __bf16) {
 // With x = |z| / sqrt 2 this gives 1 + erf(z/sqrt 2) = 2 - q for z >= 0 and
 // q for z < 0, so the negative branch keeps full relative accuracy.
 // Branch-free, about a dozen VALU operations.
-__device__ __forceinline__ float gelu_erf(float z) {
+__device__ __forceinline__ float one_plus_erf_scaled(float z) {  // 1 + erf(z / sqrt 2)
   const float x = fabsf(z) * 0.70710678118654752440f;
   const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
   float poly = fmaf(1.061405429f, t, -1.453152027f);
@@ -157,8 +169,15 @@ __device__ __forceinline__ float gelu_erf(float z) {
   poly *= t;
   // exp(-x^2) = 2^(-x^2 log2 e)
   const float q = poly * __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
-  const float one_plus_erf = z >= 0.0f ? 2.0f - q : q;
-  return 0.5f * z * one_plus_erf;
+  return z >= 0.0f ? 2.0f - q : q;
+}
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * one_plus_erf_scaled(z); }
+
+// gelu'(z) = Phi(z) + z phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi), with Phi
+// from the same erf evaluation.
+__device__ __forceinline__ float gelu_grad(float z) {
+  const float phi = 0.39894228040143267794f * __builtin_amdgcn_exp2f(-0.72134752044448170368f * z * z);
+  return fmaf(z, phi, 0.5f * one_plus_erf_scaled(z));
 }
 
 // blockIdx -> output tile.  The hardware hands consecutive workgroup ids
@@ -508,33 +527,83 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     }
   };
 
-  if (epi == EPI_DRELU_BGRAD) {
-    // dZ = mask ? acc : 0; bgrad[n] += sum over this tile's rows of dZ
+  // the tile [BM][BN] of a dtype [M, ldo] matrix into the staging buffer,
+  // row by row with 16-byte loads (zeros outside the matrix)
+  constexpr int CPR = BN / 8, RPP = NT / CPR;
+  auto load_tile = [&](const T* src) {
+    const int ch = tid % CPR;
+    const int n = n0 + ch * 8;
+    const bool vec_load = (p.ldo & 7) == 0;
+    for (int rl = tid / CPR; rl < BM; rl += RPP) {
+      const int m = m0 + rl;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (src != nullptr && m < M && n < N) {
+        const T* q = src + (size_t)m * p.ldo + n;
+        if (vec_load && n + 7 < N) {
+          v = *(const u32x4*)q;
+        } else {
+          const uint16_t* s16 = (const uint16_t*)q;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) v[e >> 1] |= (uint32_t)s16[e] << (16 * (e & 1));
+        }
+      }
+      *(u32x4*)(so + rl * (BN * 2) + ((ch ^ G::swz_o(rl)) << 4)) = v;
+    }
+  };
+  // the staged value at local row rl, local column c (4-column groups)
+  auto staged4 = [&](int rl, int c_loc) -> uint8_t* {
+    return so + rl * (BN * 2) + (((c_loc >> 3) ^ G::swz_o(rl)) << 4) + (c_loc & 7) * 2;
+  };
+
+  if (epi == EPI_DRELU_BGRAD || epi == EPI_DGELU_BGRAD) {
+    // DRELU: dZ = mask ? acc : 0.  DGELU: dZ = acc * gelu'(z), z the saved
+    // pre-activation (its tile is staged through LDS first and each dZ is
+    // written over its z).  bgrad[n] += sum over this tile's rows of dZ.
+    const bool dgelu = epi == EPI_DGELU_BGRAD;
+    if (dgelu) {
+      load_tile((const T*)p.aux);
+      __syncthreads();
+    }
     float cs[FN][16];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
       for (int r = 0; r < 16; ++r) cs[fn][r] = 0.0f;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
+    static_for<FM>([&](auto fm_c) {
+      constexpr int fm = decltype(fm_c)::value;
       const int rl = wrow0 + fm * 32 + lrow;
       const int m = m0 + rl;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int cbase = n0 + wcol0 + fn * 32;
-        const uint32_t mw = (m < M && cbase < N)
-                                ? p.aux[(size_t)m * p.aux_ld + (cbase >> 5)] >> (4 * khalf)
-                                : 0u;
         float y[16];
+        if (dgelu) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int bit = 8 * (r >> 2) + (r & 3);
-          y[r] = ((mw >> bit) & 1u) ? acc[fm][fn][r] : 0.0f;
-          cs[fn][r] += y[r];
+          for (int g = 0; g < 4; ++g) {
+            const u32x2 zw = *(const u32x2*)staged4(rl, wcol0 + fn * 32 + 4 * khalf + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint16_t zb = (uint16_t)(zw[e >> 1] >> (16 * (e & 1)));
+              const float zz = to_f32(__builtin_bit_cast(T, zb));
+              y[4 * g + e] = acc[fm][fn][4 * g + e] * gelu_grad(zz);
+            }
+          }
+        } else {
+          const uint32_t mw = (m < M && cbase < N)
+                                  ? p.aux[(size_t)m * p.aux_ld + (cbase >> 5)] >> (4 * khalf)
+                                  : 0u;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int bit = 8 * (r >> 2) + (r & 3);
+            y[r] = ((mw >> bit) & 1u) ? acc[fm][fn][r] : 0.0f;
+          }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cs[fn][r] += y[r];
         stage(rl, wcol0 + fn * 32 + 4 * khalf, y);
       }
-    }
+    });
     // sum over the 32 rows held by the lanes with the same khalf
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
@@ -562,34 +631,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // them and writes the rounded y back in place.  Partial row sums of the
     // rounded y and y^2 are kept in fp64 (the norm's variance is formed from
     // them by subtraction).
-    constexpr int CPR = BN / 8, RPP = NT / CPR;
-    {
-      const T* res = (const T*)p.residual;
-      const int ch = tid % CPR;
-      const int n = n0 + ch * 8;
-      const bool vec_load = (p.ldo & 7) == 0;
-      for (int rl = tid / CPR; rl < BM; rl += RPP) {
-        const int m = m0 + rl;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (res != nullptr && m < M && n < N) {
-          const T* src = res + (size_t)m * p.ldo + n;
-          if (vec_load && n + 7 < N) {
-            v = *(const u32x4*)src;
-          } else {
-            const uint16_t* s16 = (const uint16_t*)src;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (n + e < N) v[e >> 1] |= (uint32_t)s16[e] << (16 * (e & 1));
-          }
-        }
-        *(u32x4*)(so + rl * (BN * 2) + ((ch ^ G::swz_o(rl)) << 4)) = v;
-      }
-    }
+    load_tile((const T*)p.residual);
     __syncthreads();
     const T* bias = (const T*)p.bias;
     double* red64 = (double*)(smem + G::OUT_BYTES);  // [WN][BM][2]
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
+    static_for<FM>([&](auto fm_c) {
+      constexpr int fm = decltype(fm_c)::value;
       const int rl = wrow0 + fm * 32 + lrow;
       const int m = m0 + rl;
       double s1 = 0.0, s2 = 0.0;
@@ -599,7 +646,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int c_loc = cl + 8 * g;
-          uint8_t* at = so + rl * (BN * 2) + (((c_loc >> 3) ^ G::swz_o(rl)) << 4) + (c_loc & 7) * 2;
+          uint8_t* at = staged4(rl, c_loc);
           const u32x2 rw = *(const u32x2*)at;
           float y[4];
 #pragma unroll
@@ -625,13 +672,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         red64[(wn * BM + rl) * 2] = s1;
         red64[(wn * BM + rl) * 2 + 1] = s2;
       }
-    }
+    });
   } else {
     const bool has_bias = epi != EPI_DEFAULT;
     const bool per_col = p.bias_per_col != 0;
     const T* bias = (const T*)p.bias;
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
+    const bool gelu = epi == EPI_GELU_BIAS || epi == EPI_GELU_AUX_BIAS;
+    const bool relu = epi == EPI_RELU_BIAS || epi == EPI_RELU_AUX_BIAS;
+    static_for<FM>([&](auto fm_c) {
+      constexpr int fm = decltype(fm_c)::value;
       const int rl = wrow0 + fm * 32 + lrow;
       const int m = m0 + rl;
       const float brow = (has_bias && !per_col && m < M) ? to_f32(bias[m]) : 0.0f;
@@ -647,9 +696,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           float b = brow;
           if (has_bias && per_col) b = c < N ? to_f32(bias[c]) : 0.0f;
           const float z = acc[fm][fn][r] + b;
-          if (epi == EPI_GELU_BIAS) {
+          if (gelu) {
             y[r] = gelu_erf(z);
-          } else if (epi == EPI_RELU_BIAS || epi == EPI_RELU_AUX_BIAS) {
+          } else if (relu) {
             y[r] = z > 0.0f ? z : 0.0f;
           } else {
             y[r] = z;
@@ -658,6 +707,29 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
             bits |= 1u << (8 * (r >> 2) + 4 * khalf + (r & 3));
         }
         stage(rl, wcol0 + fn * 32 + 4 * khalf, y);
+        if (epi == EPI_GELU_AUX_BIAS && m < M) {
+          // z = acc + bias, rounded, straight into aux: per (fm, fn) a row
+          // gets 32 contiguous columns from 4 stores of lanes l and l+32
+          T* zrow = (T*)p.aux + (size_t)m * p.ldo;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int c = cgrp + 8 * g;
+            float zz[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float b = per_col ? (c + e < N ? to_f32(bias[c + e]) : 0.0f) : brow;
+              zz[e] = acc[fm][fn][4 * g + e] + b;
+            }
+            if ((p.ldo & 3) == 0 && c + 3 < N) {
+              const u32x2 w = {pack2(zz[0], zz[1], T{}), pack2(zz[2], zz[3], T{})};
+              *(u32x2*)(zrow + c) = w;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (c + e < N) zrow[c + e] = from_f32<T>(zz[e]);
+            }
+          }
+        }
         if (epi == EPI_RELU_AUX_BIAS) {
           // lanes l and l+32 hold complementary halves of row m's word
           bits |= __shfl_xor(bits, 32);
@@ -670,32 +742,35 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           }
         }
       }
-    }
+    });
   }
   __syncthreads();
 
-  // the staged tile -> out: thread t copies 16-byte chunk t % CPR of local
+  // the staged tile -> dst: thread t copies 16-byte chunk t % CPR of local
   // row t / CPR (+ RPP per pass), so a wave writes whole row segments
-  constexpr int CPR = BN / 8, RPP = NT / CPR;
-  const size_t ldo = (size_t)p.ldo;
-  const bool vec_store = (p.ldo & 7) == 0;  // 16-byte aligned rows
-  const int ch = tid % CPR;
-  const int n = n0 + ch * 8;
+  auto store_tile = [&](T* dst_base) {
+    const size_t ldo = (size_t)p.ldo;
+    const bool vec_store = (p.ldo & 7) == 0;  // 16-byte aligned rows
+    const int ch = tid % CPR;
+    const int n = n0 + ch * 8;
 #pragma unroll 4
-  for (int rl = tid / CPR; rl < BM; rl += RPP) {
-    const u32x4 v = *(const u32x4*)(so + rl * (BN * 2) + ((ch ^ G::swz_o(rl)) << 4));
-    const int m = m0 + rl;
-    if (m >= M || n >= N) continue;
-    T* dst = (T*)p.out + (size_t)m * ldo + n;
-    if (vec_store && n + 7 < N) {
-      *(u32x4*)dst = v;
-    } else {
-      uint16_t* d16 = (uint16_t*)dst;
+    for (int rl = tid / CPR; rl < BM; rl += RPP) {
+      const u32x4 v = *(const u32x4*)(so + rl * (BN * 2) + ((ch ^ G::swz_o(rl)) << 4));
+      const int m = m0 + rl;
+      if (m >= M || n >= N) continue;
+      T* dst = dst_base + (size_t)m * ldo + n;
+      if (vec_store && n + 7 < N) {
+        *(u32x4*)dst = v;
+      } else {
+        uint16_t* d16 = (uint16_t*)dst;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (n + e < N) d16[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+        for (int e = 0; e < 8; ++e)
+          if (n + e < N) d16[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+      }
     }
-  }
+  };
+  store_tile((T*)p.out);
+
 
   if (epi == EPI_BIAS_RES_SUMS) {
     const double* red64 = (const double*)(smem + G::OUT_BYTES);
@@ -712,7 +787,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       unsafeAtomicAdd(&p.stats[2 * (size_t)m + 1], s2);
     }
   }
-  if (epi == EPI_DRELU_BGRAD) {
+  if (epi == EPI_DRELU_BGRAD || epi == EPI_DGELU_BGRAD) {
     for (int c = tid; c < BN; c += NT) {
       float s = 0.0f;
 #pragma unroll

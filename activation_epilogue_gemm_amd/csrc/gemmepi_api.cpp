@@ -185,7 +185,8 @@ void describe(gemmepi_plan_s* p) {
   char buf[384];
   static const char* epis[] = {"DEFAULT",     "BIAS",        "RELU_BIAS",
                                "RELU_AUX_BIAS", "GELU_BIAS", "DRELU_BGRAD",
-                               "BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM"};
+                               "BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM",
+                               "GELU_AUX_BIAS", "DGELU_BGRAD"};
   if (p->path == PATH_DECODE) {
     snprintf(buf, sizeof(buf),
              "path=decode M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x grid=%lld waves=8 "
@@ -306,7 +307,7 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
                 (long long)M, (long long)N, (long long)K);
   if (dtype != GEMMEPI_F16 && dtype != GEMMEPI_BF16)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown dtype %d", (int)dtype);
-  if ((int)epi < GEMMEPI_EPI_DEFAULT || (int)epi > GEMMEPI_EPI_BIAS_RES_LAYERNORM)
+  if ((int)epi < GEMMEPI_EPI_DEFAULT || (int)epi > GEMMEPI_EPI_DGELU_BGRAD)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown epilogue %d", (int)epi);
   if (flags & ~kAllFlags) return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown flag bits 0x%x", flags);
   if (tile_req < -1 || tile_req >= kNumTiles)
@@ -383,19 +384,21 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
   const bool bt = p.flags & GEMMEPI_FLAG_B_TRANS;
   const bool per_col = p.flags & GEMMEPI_FLAG_BIAS_PER_COL;
   const bool unfused = p.flags & GEMMEPI_FLAG_UNFUSED;
-  const bool needs_bias = epi != EPI_DEFAULT;  // DRELU_BGRAD: bgrad output
-  const bool needs_aux = epi == EPI_RELU_AUX_BIAS || epi == EPI_DRELU_BGRAD;
+  const bool bgrad_epi = epi == EPI_DRELU_BGRAD || epi == EPI_DGELU_BGRAD;
+  const bool needs_bias = epi != EPI_DEFAULT;  // *_BGRAD: bgrad output
+  const bool needs_aux = epi == EPI_RELU_AUX_BIAS || epi == EPI_DRELU_BGRAD ||
+                         epi == EPI_GELU_AUX_BIAS || epi == EPI_DGELU_BGRAD;
 
   if (epi == EPI_BIAS_RES_RMSNORM || epi == EPI_BIAS_RES_LAYERNORM)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: norm epilogues run through execute_norm");
   if (!A || !B || !out) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: A, B and out are required");
   if (needs_bias && !bias)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs the bias pointer%s",
-                epi == EPI_DRELU_BGRAD ? " (fp32 bgrad output)" : "");
+                bgrad_epi ? " (fp32 bgrad output)" : "");
   if (needs_aux && !aux) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: this epilogue needs aux");
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(out, 16))
     return fail(GEMMEPI_ERR_MISALIGNED, "execute: A, B and out must be 16-byte aligned");
-  if (needs_bias && !aligned(bias, epi == EPI_DRELU_BGRAD ? 4 : 2))
+  if (needs_bias && !aligned(bias, bgrad_epi ? 4 : 2))
     return fail(GEMMEPI_ERR_MISALIGNED, "execute: bias misaligned");
   if (needs_aux && !aligned(aux, 16))
     return fail(GEMMEPI_ERR_MISALIGNED, "execute: aux must be 16-byte aligned");
@@ -417,7 +420,7 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
   hipError_t e = hipSuccess;
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
 
-  if (epi == EPI_DRELU_BGRAD) {
+  if (bgrad_epi) {
     e = launch_fill_f32((float*)bias, N, 0.0f, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "bgrad fill: %s", hipGetErrorString(e));
   }
@@ -457,6 +460,10 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
         break;
       case EPI_DRELU_BGRAD:
         e = launch_mask_apply(p.dtype, out, (const uint32_t*)aux, M, N, N, aux_ld, s);
+        if (e == hipSuccess) e = launch_colsum(p.dtype, out, (float*)bias, M, N, N, s);
+        break;
+      case EPI_DGELU_BGRAD:
+        e = launch_dgelu_apply(p.dtype, out, aux, M, N, N, s);
         if (e == hipSuccess) e = launch_colsum(p.dtype, out, (float*)bias, M, N, N, s);
         break;
       default:

@@ -17,9 +17,12 @@ enum Epi : int {
   EPI_DRELU_BGRAD = 5,
   EPI_BIAS_RES_RMSNORM = 6,
   EPI_BIAS_RES_LAYERNORM = 7,
-  // GEMM-kernel epilogue of both norms: y = acc + bias + residual rounded
-  // to out, fp64 partial row sums of y and y^2 added into stats
-  EPI_BIAS_RES_SUMS = 8
+  EPI_GELU_AUX_BIAS = 8,
+  EPI_DGELU_BGRAD = 9,
+  // GEMM-kernel epilogue of both norms (not a public value): y = acc + bias
+  // + residual rounded to out, fp64 partial row sums of y and y^2 added into
+  // stats
+  EPI_BIAS_RES_SUMS = 16
 };
 
 enum DType : int { DT_F16 = 0, DT_BF16 = 1 };
@@ -29,7 +32,9 @@ struct GemmArgs {
   const void* A;     // [M, lda] row-major
   const void* B;     // [K, ldb] or, transposed, [N, ldb]
   const void* bias;  // [M] or [N] in the input dtype (BIAS-type epilogues)
-  uint32_t* aux;     // packed mask [M, aux_ld] (out for RELU_AUX, in for DRELU)
+  uint32_t* aux;     // packed mask [M, aux_ld] (out for RELU_AUX, in for DRELU), or
+                     // the pre-activation z [M, ldo] in the output dtype (out for
+                     // GELU_AUX, in for DGELU)
   void* out;         // [M, ldo]
   float* bgrad;      // [N] fp32, pre-zeroed (DRELU_BGRAD)
   const void* residual;  // [M, ldo] in the output dtype or null (BIAS_RES_SUMS)
@@ -84,6 +89,9 @@ hipError_t launch_activation(int dtype, int epi, void* out, uint32_t* aux, int M
                              int aux_ld, hipStream_t s);
 hipError_t launch_mask_apply(int dtype, void* out, const uint32_t* aux, int M, int N, int ldo,
                              int aux_ld, hipStream_t s);
+// out = out * gelu'(z), z the saved pre-activation [M, ldo] (unfused DGELU)
+hipError_t launch_dgelu_apply(int dtype, void* out, const void* z, int M, int N, int ldo,
+                              hipStream_t s);
 hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_colsum(int dtype, const void* dz, float* bgrad, int M, int N, int ldo,
                          hipStream_t s);

@@ -78,8 +78,13 @@ typedef enum {
    * structural fusion"): y = acc + bias + residual, then a norm over each
    * row of y (all N columns).  Executed with gemmepi_execute_norm only. */
   GEMMEPI_EPI_BIAS_RES_RMSNORM = 6,   /* out = y / sqrt(mean(y^2) + eps) * gamma      */
-  GEMMEPI_EPI_BIAS_RES_LAYERNORM = 7  /* out = (y - mean) / sqrt(var + eps) * gamma
+  GEMMEPI_EPI_BIAS_RES_LAYERNORM = 7, /* out = (y - mean) / sqrt(var + eps) * gamma
                                          + beta; var biased (1/N)                  */
+  /* The GELU counterparts of RELU_AUX_BIAS and DRELU_BGRAD (the pages name
+   * the ReLU pair for training; these follow the same pattern for GELU). */
+  GEMMEPI_EPI_GELU_AUX_BIAS = 8, /* GELU_BIAS, plus z (rounded) kept in aux     */
+  GEMMEPI_EPI_DGELU_BGRAD = 9    /* out = acc * gelu'(z_aux); bgrad[n] = sum_m out,
+                                    gelu'(z) = Phi(z) + z phi(z)               */
 } gemmepi_epilogue_t;
 
 enum {
@@ -144,15 +149,20 @@ gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, 
  *
  *   A     [M,K] dtype, device, 16-byte aligned
  *   B     [K,N] or [N,K] (B_TRANS) dtype, device, 16-byte aligned
- *   bias  BIAS / RELU_BIAS / RELU_AUX_BIAS / GELU_BIAS: input, dtype, [M]
- *         (or [N] with BIAS_PER_COL), 2-byte aligned; required.
- *         DRELU_BGRAD: OUTPUT, fp32 [N], 4-byte aligned, overwritten with
- *         the column sums of out's unrounded values; required.
+ *   bias  BIAS / RELU_BIAS / RELU_AUX_BIAS / GELU_BIAS / GELU_AUX_BIAS:
+ *         input, dtype, [M] (or [N] with BIAS_PER_COL), 2-byte aligned;
+ *         required.
+ *         DRELU_BGRAD / DGELU_BGRAD: OUTPUT, fp32 [N], 4-byte aligned,
+ *         overwritten with the column sums of out's unrounded values;
+ *         required.
  *         DEFAULT: ignored (may be NULL).
- *   aux   RELU_AUX_BIAS: OUTPUT mask; DRELU_BGRAD: INPUT mask; else ignored.
- *         uint32 words, [M, gemmepi_aux_ld_words(N)] row-major, 16-byte
- *         aligned; column n of row m is bit (n & 31) of word (m, n >> 5);
- *         padding bits are written as 0 and ignored on input.
+ *   aux   RELU_AUX_BIAS: OUTPUT mask; DRELU_BGRAD: INPUT mask.  uint32
+ *         words, [M, gemmepi_aux_ld_words(N)] row-major, 16-byte aligned;
+ *         column n of row m is bit (n & 31) of word (m, n >> 5); padding
+ *         bits are written as 0 and ignored on input.
+ *         GELU_AUX_BIAS: OUTPUT, DGELU_BGRAD: INPUT: the pre-activation z
+ *         in the dtype, [M,N] row-major, 16-byte aligned.
+ *         Other epilogues: ignored.
  *   out   [M,N] dtype, device, 16-byte aligned; overwritten (in the UNFUSED
  *         path it is also read back by the elementwise kernels).
  *

@@ -51,8 +51,9 @@ def test_plan_validation():
     assert _plan_status(64, -1, 64) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 1 << 31) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, dtype=2) == ge.ERR_INVALID_VALUE
-    assert _plan_status(64, 64, 64, epi=8) == ge.ERR_INVALID_VALUE
-    assert _plan_status(64, 64, 64, epi=6) == ge.OK and _plan_status(64, 64, 64, epi=7) == ge.OK
+    assert _plan_status(64, 64, 64, epi=10) == ge.ERR_INVALID_VALUE
+    for epi in range(10):
+        assert _plan_status(64, 64, 64, epi=epi) == ge.OK, epi
     assert _plan_status(64, 64, 64, epi=-1) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, flags=1 << 9) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, tile=ge.num_tiles()) == ge.ERR_INVALID_VALUE
@@ -134,9 +135,17 @@ def test_execute_rejects_bad_pointers_before_any_hip_call():
         assert lib.gemmepi_execute(h, 4098, 4096, 4096, 4096, 4096, None) == ge.ERR_MISALIGNED
         # misaligned aux
         assert lib.gemmepi_execute(h, 4096, 4096, 4096, 4100, 4096, None) == ge.ERR_MISALIGNED
-    with ge.plan(64, 64, 64, "f16", "DRELU_BGRAD", 0) as p:
-        # bgrad must be 4-byte aligned
-        assert lib.gemmepi_execute(p._h, 4096, 4096, 4098, 4096, 4096, None) == ge.ERR_MISALIGNED
+    for epi in ("DRELU_BGRAD", "DGELU_BGRAD"):
+        with ge.plan(64, 64, 64, "f16", epi, 0) as p:
+            # bgrad must be 4-byte aligned
+            assert lib.gemmepi_execute(p._h, 4096, 4096, 4098, 4096, 4096, None) == ge.ERR_MISALIGNED
+            # the saved mask or z is required
+            assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, None, 4096, None) == \
+                ge.ERR_INVALID_VALUE
+    with ge.plan(64, 64, 64, "f16", "GELU_AUX_BIAS", 0) as p:
+        # z output: required, 16-byte aligned
+        assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, None, 4096, None) == ge.ERR_INVALID_VALUE
+        assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, 4104, 4096, None) == ge.ERR_MISALIGNED
     assert lib.gemmepi_execute(None, 4096, 4096, 4096, 4096, 4096, None) == ge.ERR_INVALID_VALUE
     assert lib.gemmepi_stream_read(None, 4096, 4096, None) == ge.ERR_INVALID_VALUE
     assert lib.gemmepi_stream_read(4096, 0, 4096, None) == ge.ERR_INVALID_VALUE

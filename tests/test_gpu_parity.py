@@ -17,7 +17,7 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import GpuRun, check_bgrad, check_mask, check_out
+from parity import BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check_out, check_zaux
 
 pytestmark = pytest.mark.gpu
 
@@ -34,12 +34,15 @@ def oracle_of(c, rows=None, A_bits=None):
 
 
 def run_and_check(c, flags=0, tile=-1, exact=False, guard=0, label=""):
+    """exact: integer inputs, so every result that is a rounding of an exact
+    sum is compared bit for bit; results that go through GELU or its
+    derivative (out of the GELU epilogues, DGELU's bgrad) use the tolerance."""
     r = GpuRun(c, flags=flags, tile=tile, guard=guard)
     say(label, c.name, r.info)
     r.run()
     ref = oracle_of(c)
     got = r.out_bits()
-    if exact:
+    if exact and c.epilogue not in GELU_EPIS:
         if not np.array_equal(got, ref.out):
             bad = np.argwhere(got != ref.out)[:5]
             raise AssertionError(f"{label} {c.name} [{r.info}]: {int((got != ref.out).sum())} "
@@ -54,13 +57,20 @@ def run_and_check(c, flags=0, tile=-1, exact=False, guard=0, label=""):
             assert np.array_equal(words, ref.mask), f"{label} {c.name}: mask differs"
         else:
             check_mask(c, words, ref, label=label)
-    if c.epilogue == "DRELU_BGRAD":
-        bg = r.bgrad()
+    if c.epilogue == "GELU_AUX_BIAS":
+        zb = r.zaux_bits()
         if exact:
+            assert np.array_equal(zb, ref.zaux), f"{label} {c.name}: z aux differs " \
+                f"{np.argwhere(zb != ref.zaux)[:5].tolist()}"
+        else:
+            check_zaux(c, zb, ref, label=label)
+    if c.epilogue in BGRAD_EPIS:
+        bg = r.bgrad()
+        if exact and c.epilogue == "DRELU_BGRAD":
             assert np.array_equal(bg, ref.bgrad), f"{label} {c.name}: bgrad differs " \
                 f"{np.argwhere(bg != ref.bgrad)[:5].ravel().tolist()}"
         else:
-            check_bgrad(c, bg, ref, label=label)
+            check_bgrad(c, bg, ref, label=label, unfused=bool(flags & ge.FLAG_UNFUSED))
     assert r.guards_intact(), f"{label} {c.name}: write outside the output buffers"
     r.close()
 
@@ -82,7 +92,7 @@ def test_integer_exact_every_tile(tile, b_trans, dtype):
         if epi == "GELU_BIAS":
             continue  # not exact by nature; covered with tolerance below
         for per_col in (False, True):
-            if epi in ("DEFAULT", "DRELU_BGRAD") and per_col:
+            if (epi == "DEFAULT" or epi in BGRAD_EPIS) and per_col:
                 continue
             c = wl.random_case(M, N, K, dtype, epi, b_trans, per_col, 100 + 7 * ei + per_col,
                                kind="int")
@@ -99,7 +109,7 @@ def test_integer_exact_every_tile(tile, b_trans, dtype):
 def test_tolerance_every_tile_gelu_and_normal_inputs(tile, b_trans):
     M, N, K = 260, 200, 328
     for dtype in ("f16", "bf16"):
-        for epi in ("GELU_BIAS", "RELU_AUX_BIAS", "DRELU_BGRAD"):
+        for epi in ("GELU_BIAS", "RELU_AUX_BIAS", "DRELU_BGRAD", "GELU_AUX_BIAS", "DGELU_BGRAD"):
             c = wl.random_case(M, N, K, dtype, epi, b_trans, b_trans, 555 + tile)
             run_and_check(c, tile=tile, label=f"tile{tile}")
 
@@ -113,6 +123,7 @@ def test_unfused_matches_oracle(epi, dtype):
         run_and_check(c, flags=ge.FLAG_UNFUSED, label="unfused")
     if dtype == "f16" and epi != "GELU_BIAS":
         # small integers stay exact through the unfused fp16 intermediates
+        # (GELU results themselves are held to the tolerance)
         c = wl.random_case(300, 264, 200, dtype, epi, False, False, 950, kind="int")
         run_and_check(c, flags=ge.FLAG_UNFUSED, exact=True, guard=64, label="unfused-int")
 
@@ -147,7 +158,7 @@ def test_edge_shapes(shape):
     for epi in EPIS:
         b_trans = (N % 8 != 0) or (M % 2 == 1)
         c = wl.random_case(M, N, K, "f16", epi, b_trans, False, 11 + M + N + K, kind="int")
-        run_and_check(c, exact=(epi != "GELU_BIAS"), guard=16, label="edge")
+        run_and_check(c, exact=True, guard=16, label="edge")
 
 
 def test_repeatable_and_stable():
@@ -199,10 +210,10 @@ def test_config2_ffn_full(variant):
 def _large(c, rows_count=4096):
     """4096 seed-chosen rows (always 0 and M-1) of out / mask, all of bgrad."""
     import torch
-    cfg = 4 if c.epilogue == "DRELU_BGRAD" else 3
+    cfg = 4 if c.epilogue in BGRAD_EPIS else 3
     rows = wl.sample_rows(c.M, rows_count, wl.row_sample_seed(cfg))
     B = c.host_B()
-    if c.epilogue == "DRELU_BGRAD":
+    if c.epilogue in BGRAD_EPIS:
         ref = O.gemm_epilogue(c.host_A(), B, None, c.aux, c.M, c.N, c.K, c.dtype, c.epilogue,
                               False, False, rows=rows)
     else:
@@ -216,8 +227,11 @@ def _large(c, rows_count=4096):
         if c.epilogue == "RELU_AUX_BIAS":
             n = check_mask(c, r.aux_words(rows), ref, label=f"large-{flags}")
             say("mask bits excused", n, "of", ref.z.size)
-        if c.epilogue == "DRELU_BGRAD":
-            check_bgrad(c, r.bgrad(), ref, label=f"large-{flags}")
+        if c.epilogue == "GELU_AUX_BIAS":
+            check_zaux(c, r.zaux_bits(rows), ref, label=f"large-{flags}")
+        if c.epilogue in BGRAD_EPIS:
+            check_bgrad(c, r.bgrad(), ref, label=f"large-{flags}",
+                        unfused=bool(flags & ge.FLAG_UNFUSED))
         r.close()
         del r
         torch.cuda.empty_cache()
@@ -230,3 +244,14 @@ def test_config3_relu_aux_full(dtype):
 
 def test_config4_drelu_bgrad_full():
     _large(wl.config4_drelu_bgrad())
+
+
+def test_dgelu_bgrad_full():
+    """The GELU backward at the DRELU backward's shape (dY[8192,16384],
+    W[16384,4096]) with a saved z of the same size."""
+    _large(wl.config4_dgelu_bgrad())
+
+
+def test_gelu_aux_full():
+    """The GELU forward that saves z, at the ReLU-aux forward's shape."""
+    _large(wl.config3_gelu_aux())

@@ -163,13 +163,14 @@ class GemmCase:
     N: int
     K: int
     dtype: str
-    epilogue: str            # DEFAULT BIAS RELU_BIAS RELU_AUX_BIAS GELU_BIAS DRELU_BGRAD
+    epilogue: str            # a key of the binding's EPILOGUES (not the norms)
     b_trans: bool            # B stored [N,K] (K contiguous) instead of [K,N]
     bias_per_col: bool       # bias indexed by n instead of m
     A: np.ndarray = None     # uint16 bits [M,K]
     B: np.ndarray = None     # uint16 bits [K,N] or [N,K]
     bias: Optional[np.ndarray] = None   # uint16 bits [M] or [N]
-    aux: Optional[np.ndarray] = None    # uint32 [M, aux_ld_words(N)] (input mask)
+    aux: Optional[np.ndarray] = None    # DRELU: uint32 mask [M, aux_ld_words(N)];
+                                        # DGELU: uint16 bits of the saved z [M, N]
 
     @property
     def flops(self) -> float:
@@ -283,6 +284,27 @@ def config4_drelu_bgrad(dtype: str = F16, device="cuda", M: int = 8192, N: int =
     c.A_dev = device_normal((M, K), seed_of(4, 0), 1.0 / 128.0, dtype, device)
     c.B_dev = device_normal((K, N), seed_of(4, 1), 1.0 / 128.0, dtype, device)
     c.aux = random_mask(M, N, seed_of(4, 2))
+    return c
+
+
+def config3_gelu_aux(dtype: str = F16, device="cuda", M: int = 65536, N: int = 8192,
+                     K: int = 16384) -> DeviceCase:
+    """C3's operands with the GELU epilogue that also saves z = A B + bias."""
+    c = config3_relu_aux(dtype, device, M, N, K)
+    c.name = f"c3_gelu_aux_{dtype}"
+    c.epilogue = "GELU_AUX_BIAS"
+    return c
+
+
+def config4_dgelu_bgrad(dtype: str = F16, device="cuda", M: int = 8192, N: int = 4096,
+                        K: int = 16384) -> DeviceCase:
+    """dZ = (dY[M,K] W[K,N]) * gelu'(z) and bgrad[N] = column sums of dZ;
+    dY, W ~ N(0,1)/128 as in the ReLU backward, the saved pre-activation
+    z ~ N(0, 1.5^2) in the storage dtype, [M, N]."""
+    c = DeviceCase(f"c4_dgelu_bgrad_{dtype}", M, N, K, dtype, "DGELU_BGRAD", False, False)
+    c.A_dev = device_normal((M, K), seed_of(4, 0), 1.0 / 128.0, dtype, device)
+    c.B_dev = device_normal((K, N), seed_of(4, 1), 1.0 / 128.0, dtype, device)
+    c.aux = normal((M, N), seed_of(4, 3), 1.5, dtype)
     return c
 
 

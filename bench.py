@@ -17,6 +17,11 @@ TFLOP/s or GB/s, fraction of the roofline and fusion speedup; the roofline
 of the dominant kernel (the C3 fp16 GEMM, timed with HIP events on the stream
 it is launched on); and the CPU oracle timed on a bounded sample on this
 host.  Inputs are seeded synthetic data already resident in HBM.
+
+Timed beside the step but outside it ("in_step": false):
+  C5  GEMM + bias + residual + LayerNorm / RMSNorm, x[2048,11008] W[4096,11008]^T
+  C6  DGELU_BGRAD   C4's shape with a saved z[8192,4096] in place of the mask
+  C7  GELU_AUX_BIAS C3's fp16 shape, writing gelu(z) and z
 """
 from __future__ import annotations
 
@@ -46,7 +51,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--reps", type=int, default=0, help="reps per workload timing (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of workloads (c0,c1,c2,c3,c4)")
+    ap.add_argument("--only", default="", help="comma list of workloads (suite c0..c4, extras c5..c7)")
     ap.add_argument("--profile-traffic", action="store_true",
                     help="only run a plain 1 GiB copy (calibration) and the C3 fp16 fused kernel "
                          "twice each, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
@@ -88,14 +93,17 @@ class Workload:
             c.B_dev if getattr(c, "B_dev", None) is not None else upload_bits(c.B, c.dtype, dev))
         self.out = out if out is not None else torch.empty(c.M, c.N, dtype=tdt, device=dev)
         self.bias = self.aux = None
-        if c.epilogue == "DRELU_BGRAD":
+        if c.epilogue in ("DRELU_BGRAD", "DGELU_BGRAD"):
             self.bias = torch.empty(c.N, dtype=torch.float32, device=dev)
-            self.aux = upload_words(c.aux, dev)
+            self.aux = (upload_words(c.aux, dev) if c.epilogue == "DRELU_BGRAD"
+                        else upload_bits(c.aux, c.dtype, dev))
         else:
             if c.bias is not None:
                 self.bias = upload_bits(c.bias, c.dtype, dev)
             if c.epilogue == "RELU_AUX_BIAS":
                 self.aux = torch.empty(c.M, ge.aux_ld_words(c.N), dtype=torch.int32, device=dev)
+            if c.epilogue == "GELU_AUX_BIAS":
+                self.aux = torch.empty(c.M, c.N, dtype=tdt, device=dev)
         f = flags | (ge.FLAG_B_TRANS if c.b_trans else 0) | (ge.FLAG_BIAS_PER_COL if c.bias_per_col else 0)
         self.fused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f)
         self.unfused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f | ge.FLAG_UNFUSED)
@@ -106,7 +114,7 @@ class Workload:
         if self.bias is not None:
             self.bytes += self.bias.numel() * self.bias.element_size()
         if self.aux is not None:
-            self.bytes += self.aux.numel() * 4
+            self.bytes += self.aux.numel() * self.aux.element_size()
         self.rotation = None  # list of (A, B, out) for cache-cold decode timing
 
     def run(self, unfused=False, i=0):
@@ -150,14 +158,20 @@ class NormWorkload:
 def build_extras(only):
     """Workloads of the 'next' rows, timed and reported beside the suite but
     not part of its step: GEMM + bias + residual + LayerNorm / RMSNorm at the
-    2048-token FFN down-projection shape."""
+    2048-token FFN down-projection shape (c5); the GELU backward at the ReLU
+    backward's shape (c6); the GELU forward that saves z at the ReLU-aux
+    forward's shape (c7)."""
     import workloads as wl
-    sel = set(only.split(",")) if only else {"c5"}
+    sel = set(only.split(",")) if only else {"c5", "c6", "c7"}
     extras = []
     if "c5" in sel:
         for norm in ("LAYERNORM", "RMSNORM"):
             extras.append(NormWorkload(f"c5_ffn_down_res_{norm.lower()}",
                                        wl.config5_ffn_down_norm(norm)))
+    if "c6" in sel:
+        extras.append(Workload("c6_dgelu_bgrad", wl.config4_dgelu_bgrad()))
+    if "c7" in sel:
+        extras.append(Workload("c7_gelu_aux_f16", wl.config3_gelu_aux("f16")))
     return extras
 
 

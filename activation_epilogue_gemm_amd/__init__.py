@@ -9,6 +9,7 @@ The names follow the C ABI in ``include/gemmepi.h``:
 
     p = plan(M, N, K, "f16", "RELU_AUX_BIAS", flags)     # gemmepi_plan
     p.execute(A, B, bias, aux, out)                       # gemmepi_execute
+                                      # (gemmepi_execute_ws for split-K plans)
     p.info()                                              # gemmepi_plan_info
     p.destroy()  /  with plan(...) as p: ...              # gemmepi_plan_destroy
 
@@ -47,6 +48,7 @@ FLAG_BIAS_PER_COL = 1 << 1
 FLAG_UNFUSED = 1 << 2
 FLAG_VALIDATE = 1 << 3
 FLAG_NO_DECODE = 1 << 4
+FLAG_SPLIT_K = 1 << 5
 
 
 class GemmEpiError(RuntimeError):
@@ -80,6 +82,13 @@ def _load():
     lib.gemmepi_plan_tiled.restype = ctypes.c_int
     lib.gemmepi_execute.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.gemmepi_execute.restype = ctypes.c_int
+    lib.gemmepi_plan_split.argtypes = [ctypes.POINTER(vp), i64, i64, i64, ctypes.c_int,
+                                       ctypes.c_int, u32, i32, i32]
+    lib.gemmepi_plan_split.restype = ctypes.c_int
+    lib.gemmepi_workspace_bytes.argtypes = [vp]
+    lib.gemmepi_workspace_bytes.restype = ctypes.c_size_t
+    lib.gemmepi_execute_ws.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.gemmepi_execute_ws.restype = ctypes.c_int
     lib.gemmepi_plan_destroy.argtypes = [vp]
     lib.gemmepi_plan_destroy.restype = ctypes.c_int
     lib.gemmepi_plan_info.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
@@ -182,16 +191,20 @@ class Plan:
     :meth:`destroy`; plans for the same arguments share one cache entry."""
 
     def __init__(self, M: int, N: int, K: int, dtype: str = "f16", epilogue: str = "BIAS",
-                 flags: int = 0, tile: int = -1):
+                 flags: int = 0, tile: int = -1, splits: Optional[int] = None):
         lib = _load()
         self.M, self.N, self.K = int(M), int(N), int(K)
         self.dtype, self.epilogue, self.flags, self.tile = dtype, epilogue, int(flags), int(tile)
+        self._ws = None  # workspace allocated here when execute() is given none
         if dtype not in DTYPES:
             raise ValueError(f"dtype must be one of {list(DTYPES)}")
         if epilogue not in EPILOGUES:
             raise ValueError(f"epilogue must be one of {list(EPILOGUES)}")
         h = ctypes.c_void_p()
-        if tile < 0:
+        if splits is not None:
+            st = lib.gemmepi_plan_split(ctypes.byref(h), self.M, self.N, self.K, DTYPES[dtype],
+                                        EPILOGUES[epilogue], self.flags, self.tile, int(splits))
+        elif tile < 0:
             st = lib.gemmepi_plan(ctypes.byref(h), self.M, self.N, self.K, DTYPES[dtype],
                                   EPILOGUES[epilogue], self.flags)
         else:
@@ -202,17 +215,44 @@ class Plan:
 
     # ---- the C calls ----------------------------------------------------
     def execute(self, A: Pointer, B: Pointer, bias: Pointer = None, aux: Pointer = None,
-                out: Pointer = None, stream=None, check: bool = True) -> None:
-        """Enqueue one execution (gemmepi_execute).  Tensor arguments are
+                out: Pointer = None, stream=None, check: bool = True, workspace: Pointer = None,
+                workspace_nbytes: Optional[int] = None) -> None:
+        """Enqueue one execution (gemmepi_execute, or gemmepi_execute_ws when
+        the plan splits K or a workspace is given).  Tensor arguments are
         checked for dtype, shape, contiguity and device first (``check``);
-        raw integer pointers are passed through unchecked."""
+        raw integer pointers are passed through unchecked.  A split-K plan
+        given no workspace uses a zeroed one that the Plan allocates once."""
         if self._h is None:
             raise ValueError("plan destroyed")
         if check:
             self._check_tensors(A, B, bias, aux, out)
-        st = _load().gemmepi_execute(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(aux), _ptr(out),
-                                     _stream_handle(stream, A, B, out))
-        _check(st, "gemmepi_execute")
+        need = self.workspace_bytes()
+        if need == 0 and workspace is None:
+            st = _load().gemmepi_execute(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(aux),
+                                         _ptr(out), _stream_handle(stream, A, B, out))
+            _check(st, "gemmepi_execute")
+            return
+        if workspace is None:
+            workspace = self._own_workspace(need, out)
+        nbytes = workspace_nbytes if workspace_nbytes is not None else (
+            need if isinstance(workspace, int) else workspace.numel() * workspace.element_size())
+        st = _load().gemmepi_execute_ws(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(aux),
+                                        _ptr(out), _ptr(workspace), int(nbytes),
+                                        _stream_handle(stream, A, B, out))
+        _check(st, "gemmepi_execute_ws")
+
+    def workspace_bytes(self) -> int:
+        """gemmepi_workspace_bytes: device workspace this plan needs (0 unless
+        it splits K)."""
+        return int(_load().gemmepi_workspace_bytes(self._h))
+
+    def _own_workspace(self, need: int, like):
+        """A zeroed workspace kept with the plan (memory plumbing only)."""
+        if self._ws is None or self._ws.numel() < need:
+            import torch
+            dev = like.device if hasattr(like, "device") else torch.device("cuda")
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+        return self._ws
 
     def execute_norm(self, A: Pointer, B: Pointer, bias: Pointer, residual: Pointer,
                      gamma: Pointer, beta: Pointer, eps: float, stats: Pointer, out: Pointer,
@@ -350,9 +390,9 @@ def norm_stats_bytes(M: int) -> int:
 
 
 def plan(M: int, N: int, K: int, dtype: str = "f16", epilogue: str = "BIAS", flags: int = 0,
-         tile: int = -1) -> Plan:
-    """gemmepi_plan / gemmepi_plan_tiled."""
-    return Plan(M, N, K, dtype, epilogue, flags, tile)
+         tile: int = -1, splits: Optional[int] = None) -> Plan:
+    """gemmepi_plan / gemmepi_plan_tiled / gemmepi_plan_split (splits given)."""
+    return Plan(M, N, K, dtype, epilogue, flags, tile, splits)
 
 
 def execute(p: Plan, A, B, bias=None, aux=None, out=None, stream=None) -> None:

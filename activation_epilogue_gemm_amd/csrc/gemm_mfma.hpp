@@ -52,6 +52,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __bf16 bf16x4_t __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -190,9 +191,8 @@ __device__ __forceinline__ float gelu_grad(float z) {
 //    Infinity Cache instead of each reading them from HBM.
 //  * Otherwise (shapes that do not divide): with xcd_remap each XCD walks a
 //    contiguous run of the tile order, grouped by `group_m` tile rows.
-__device__ __forceinline__ void tile_coords(const GemmArgs& p, int& tm, int& tn) {
-  int bid = blockIdx.x;
-  const int nb = gridDim.x;
+//  Tile id `bid` of `nb` (the workgroup id, or its tile under split-K).
+__device__ __forceinline__ void tile_coords(const GemmArgs& p, int bid, int nb, int& tm, int& tn) {
   if (p.sb_m > 0) {
     const int x = bid & 7;                 // XCD of this workgroup
     const int j = bid >> 3;                // its index on that XCD
@@ -279,8 +279,11 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int split = p.splits > 1 ? (int)blockIdx.x / ntiles : 0;
+  const int tile_id = (int)blockIdx.x - split * ntiles;
   int tm, tn;
-  tile_coords(p, tm, tn);
+  tile_coords(p, tile_id, ntiles, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int M = p.M, N = p.N, K = p.K;
 
@@ -294,6 +297,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   // bit j set when load j lies beyond K in the last slab.
   const int KT = (K + BK - 1) / BK;
   const int k_last = (KT - 1) * BK;
+  // this workgroup's slabs [kt_begin, kt_end): all of K, or one split of it
+  const int kt_begin = p.splits > 1 ? split * p.kt_split : 0;
+  const int kt_end = p.splits > 1 ? min(KT, kt_begin + p.kt_split) : KT;
   uint32_t tail_bits = 0;
   uint32_t a_off[A_CH];
 #pragma unroll
@@ -326,12 +332,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
                             : (const uint8_t*)p.B + (size_t)n0 * 2;
 
   // load j (0 <= j < LPS) of this wave's share of slab kt into stage st:
-  // j < A_CH are A blocks, the rest B blocks.  A slab kt >= KT is a
+  // j < A_CH are A blocks, the rest B blocks.  A slab kt >= kt_end is a
   // placeholder: its loads read nothing and write zeros into a stage that
   // no later slab uses, which keeps the count of loads per slab uniform.
   auto issue_one = [&](int kt, uint8_t* st, int j) {
     const uint32_t st_addr = __builtin_amdgcn_readfirstlane(lds_addr_of(st));
-    const bool none = kt >= KT;
+    const bool none = kt >= kt_end;
     const int k0 = none ? 0 : kt * BK;
     // branch-free: bit 31 from "placeholder" (uniform) or "beyond K" (lane)
     const uint32_t kill = (none ? kOOB : 0u) | ((kt == KT - 1 ? (tail_bits >> j) & 1u : 0u) << 31);
@@ -435,9 +441,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     }
   };
 
-  // prologue: slabs 0 .. NS-2 (or placeholders) in flight, wait for slab 0
+  // prologue: the first NS-1 slabs (or placeholders) in flight, wait for the first
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s, smem + s * G::STAGE);
+  for (int s = 0; s < NS - 1; ++s) issue(kt_begin + s, smem + s * G::STAGE);
   wait_vmcnt<(NS - 2) * G::LPS>();
   __syncthreads();
   int cur = 0;                      // stage of slab kt
@@ -455,7 +461,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // and read again in phase 2s + 2 NS, after both groups' waits for it.
     const int grp = wave >> 2;
     if (grp == 1) phase_barrier();
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
       V8 af[KS][FM], bf[KS][FN];
       const uint8_t* st = smem + cur * G::STAGE;
 #pragma unroll
@@ -489,9 +495,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     wait_vmcnt<0>();
     __syncthreads();
   } else
-  for (int kt = 0; kt < KT; ++kt) {
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
     // the stage of slab kt-1 is free: every wave passed the last barrier
-    const bool more = kt + NS - 1 < KT;
+    const bool more = kt + NS - 1 < kt_end;
     if (more) issue(kt + NS - 1, smem + nxt * G::STAGE);
     compute(smem + cur * G::STAGE);
     // slab kt+1 must have landed; slabs kt+2 .. kt+NS-1 may stay in flight
@@ -502,6 +508,70 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     __syncthreads();
     cur = (cur + 1 == NS) ? 0 : cur + 1;
     nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
+  }
+
+  // ---- split-K: partial tiles through the workspace ---------------------------
+  // Each split writes its fp32 accumulators to its slot, element-major
+  // (element q of thread t at q * NT + t, so each store or load of a wave is
+  // one contiguous 256 bytes).  The slot is written and read with
+  // agent-scope atomic stores and loads, which are coherent across the XCDs'
+  // L2 caches on their own; a fence would instead write back and invalidate
+  // the whole L2 of the XCD, which measured ~0.7 us per workgroup.  A split
+  // waits for its stores to complete, then counts its arrival; the split
+  // that arrives last sums all slots in split order (the result does not
+  // depend on arrival order), resets the count and runs the epilogue.
+  // Nothing waits on another workgroup, so no ordering of the workgroups
+  // can stall the grid.
+  if (p.splits > 1) {
+    constexpr int QE = FM * FN * 16;  // floats per thread
+    float* const slots = p.ws + (size_t)tile_id * p.splits * (BM * BN);
+    float* const own = slots + (size_t)split * (QE * NT);
+    static_for<FM>([&](auto fm_c) {
+      constexpr int fm = decltype(fm_c)::value;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(own + ((fm * FN + fn) * 16 + r) * NT + tid, acc[fm][fn][r],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    });
+    wait_vmcnt<0>();  // this thread's slot stores are complete
+    __syncthreads();  // ... and every thread's
+    __shared__ uint32_t s_last;
+    if (tid == 0) {
+      const uint32_t before = __hip_atomic_fetch_add(&p.counters[tile_id], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t last = before == (uint32_t)(p.splits - 1) ? 1u : 0u;
+      if (last) __hip_atomic_store(&p.counters[tile_id], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = last;
+    }
+    __syncthreads();
+    if (s_last == 0u) return;  // uniform over the workgroup
+    // one slot per pass, in steps of 16 or 32 independent loads (hoisting
+    // all loads of a slot would spill the accumulators)
+    constexpr int FNG = FN > 2 ? 1 : FN;  // accumulator blocks per step
+    for (int s = 0; s < p.splits; ++s) {
+      const float* src = slots + (size_t)s * (QE * NT);
+      static_for<FM>([&](auto fm_c) {
+        constexpr int fm = decltype(fm_c)::value;
+#pragma unroll
+        for (int f0 = 0; f0 < FN; f0 += FNG) {
+          float v[FNG][16];
+#pragma unroll
+          for (int j = 0; j < FNG; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              v[j][r] = __hip_atomic_load(src + ((fm * FN + f0 + j) * 16 + r) * NT + tid,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int j = 0; j < FNG; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[fm][f0 + j][r] = (s == 0 ? 0.0f : acc[fm][f0 + j][r]) + v[j][r];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    }
   }
 
   // ---- epilogue on the accumulators -----------------------------------------
@@ -805,7 +875,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
   static_assert(SCHED != 1 || (BK / 16) * (BM / WM / 32) * (BN / WN / 32) >=
                                   GemmTile<BM, BN, BK, WM, WN, NS>::LPS,
                 "ping-pong issues one load after each MFMA of a compute phase");
-  const int blocks = a.tiles_m * a.tiles_n;
+  const int blocks = a.tiles_m * a.tiles_n * (a.splits > 1 ? a.splits : 1);
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, NS, BT, SCHED>), dim3(blocks), dim3(WM * WN * 64),
                      0, s, a);
   return hipGetLastError();

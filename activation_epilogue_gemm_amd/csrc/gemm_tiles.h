@@ -13,10 +13,9 @@
 #define GEMMEPI_TILES(X)         \
   X(0, 256, 256, 64, 2, 4, 2, 0) \
   X(1, 256, 256, 32, 2, 4, 4, 0) \
-  X(2, 256, 256, 32, 2, 2, 4, 0) \
-  X(3, 256, 128, 64, 2, 2, 3, 0) \
-  X(4, 128, 128, 64, 2, 2, 3, 0) \
-  X(5, 128, 64, 64, 2, 2, 3, 0)  \
-  X(6, 64, 64, 64, 2, 2, 3, 0)   \
-  X(7, 256, 256, 32, 2, 4, 4, 1) \
-  X(8, 256, 128, 64, 4, 2, 3, 1)
+  X(2, 256, 128, 64, 2, 2, 3, 0) \
+  X(3, 128, 128, 64, 2, 2, 3, 0) \
+  X(4, 128, 64, 64, 2, 2, 3, 0)  \
+  X(5, 64, 64, 64, 2, 2, 3, 0)   \
+  X(6, 256, 256, 32, 2, 4, 4, 1) \
+  X(7, 256, 128, 64, 4, 2, 3, 1)

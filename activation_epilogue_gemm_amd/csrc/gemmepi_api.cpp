@@ -38,8 +38,8 @@ const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 // kNumCU * occ tiles; in one round a CU holds up to `occ` tiles that share
 // its MFMA units, so
 //   est = rounds * min(occ, ceil(tiles / kNumCU)) * BM * BN / eff.
-static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.86, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95};
-static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 1, 2, 3, 1, 1};
+static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95};
+static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 2, 3, 1, 1};
 constexpr int kNumCU = 256;
 
 hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s) {
@@ -59,11 +59,13 @@ struct gemmepi_plan_s {
   int dtype, epi;
   uint32_t flags;
   int tile_req;
+  int splits_req;  // -1 from the flags, 0 chosen, >= 1 requested
   int path;
   int tile;
   int tiles_m, tiles_n, group_m, xcd_remap;
   int sb_m, sb_n, xcd_m, xcd_n;
   int tuned;  // tile taken from a measured autotune result
+  int splits, kt_split;  // split-K: K ranges per tile, k slabs per range
   int k_per_wave;
   int refs;
   std::string info;
@@ -71,7 +73,7 @@ struct gemmepi_plan_s {
 
 namespace {
 
-using Key = std::tuple<int64_t, int64_t, int64_t, int, int, uint32_t, int>;
+using Key = std::tuple<int64_t, int64_t, int64_t, int, int, uint32_t, int, int>;
 
 std::mutex g_mu;
 std::map<Key, gemmepi_plan_s*>& cache() {
@@ -150,7 +152,14 @@ gemmepi_status_t fail(gemmepi_status_t s, const char* fmt, ...) {
 
 constexpr uint32_t kAllFlags = GEMMEPI_FLAG_B_TRANS | GEMMEPI_FLAG_BIAS_PER_COL |
                                GEMMEPI_FLAG_UNFUSED | GEMMEPI_FLAG_VALIDATE |
-                               GEMMEPI_FLAG_NO_DECODE;
+                               GEMMEPI_FLAG_NO_DECODE | GEMMEPI_FLAG_SPLIT_K;
+constexpr int kMaxSplits = 64;
+// Split-K cost model, fitted to a measured (tile, splits) sweep on one
+// MI355X: a split unit pays for its partial-tile round trip about as much
+// as kSplitCost k-steps of MFMA work on its tile, and a split plan must be
+// estimated at least kSplitGain faster than the best unsplit plan.
+constexpr double kSplitCost = 200.0;
+constexpr double kSplitGain = 0.95;
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
 
 bool log_enabled() {
@@ -161,24 +170,79 @@ bool log_enabled() {
   return v != 0;
 }
 
+// Split-K ranges actually used for a request of `splits`: whole k slabs
+// per range, no empty range.
+void split_shape(int64_t K, int bk, int splits, int* eff_splits, int* kt_split) {
+  const int64_t KT = (K + bk - 1) / bk;
+  int64_t s = splits < 1 ? 1 : splits;
+  if (s > KT) s = KT;
+  const int64_t per = (KT + s - 1) / s;
+  *kt_split = (int)per;
+  *eff_splits = (int)((KT + per - 1) / per);
+}
+
+// Estimated time of tile t with `splits` K ranges: the units (tile, range)
+// run in rounds of kNumCU * occ; a CU's share of a round costs its units'
+// MFMA work (BM * BN * k) over the tile's efficiency, plus, when K is
+// split, the partial-tile round trip (all splits' partials are read by the
+// last one: kSplitCost * BM * BN * splits).
+double tile_estimate(int t, int64_t M, int64_t N, int64_t K, int splits) {
+  const TileCfg& c = kTiles[t];
+  int s = 1, per = 0;
+  split_shape(K, c.bk, splits, &s, &per);
+  const int64_t units = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn) * s;
+  const int64_t slots = (int64_t)kNumCU * kTileOcc[t];
+  const int64_t rounds = (units + slots - 1) / slots;
+  const int64_t per_cu = (units + kNumCU - 1) / kNumCU;
+  const int64_t share = per_cu < kTileOcc[t] ? per_cu : kTileOcc[t];
+  double unit = (double)c.bm * c.bn * per * c.bk / kTileEff[t];
+  if (s > 1) unit += kSplitCost * c.bm * c.bn * s;
+  return (double)rounds * share * unit;
+}
+
 int choose_tile(int64_t M, int64_t N, int64_t K) {
-  (void)K;
   int best = 0;
   double best_est = 0.0;
   for (int t = 0; t < kNumTiles; ++t) {
-    const TileCfg& c = kTiles[t];
-    const int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const int64_t slots = (int64_t)kNumCU * kTileOcc[t];
-    const int64_t rounds = (tiles + slots - 1) / slots;
-    const int64_t per_cu = (tiles + kNumCU - 1) / kNumCU;
-    const int64_t share = per_cu < kTileOcc[t] ? per_cu : kTileOcc[t];
-    const double est = (double)rounds * share * c.bm * c.bn / kTileEff[t];
+    const double est = tile_estimate(t, M, N, K, 1);
     if (t == 0 || est < best_est) {
       best = t;
       best_est = est;
     }
   }
   return best;
+}
+
+// Tile (when tile < 0) and split count for a split-K-enabled plan: the
+// best unsplit estimate, unless some split count in {2, 3, 4, 6, 8, 16}
+// is estimated kSplitGain faster.
+void choose_split(int64_t M, int64_t N, int64_t K, int* tile, int* splits) {
+  const int t0 = *tile < 0 ? 0 : *tile, t1 = *tile < 0 ? kNumTiles : *tile + 1;
+  static const int kCand[] = {2, 3, 4, 6, 8, 16};
+  int bt = t0, bst = t0, bss = 1;
+  double best1 = 0.0, bests = 0.0;
+  for (int t = t0; t < t1; ++t) {
+    const double e1 = tile_estimate(t, M, N, K, 1);
+    if (t == t0 || e1 < best1) {
+      best1 = e1;
+      bt = t;
+    }
+    for (int s : kCand) {
+      const double es = tile_estimate(t, M, N, K, s);
+      if (bests == 0.0 || es < bests) {
+        bests = es;
+        bst = t;
+        bss = s;
+      }
+    }
+  }
+  if (bests < kSplitGain * best1) {
+    *tile = bst;
+    *splits = bss;
+  } else {
+    *tile = bt;
+    *splits = 1;
+  }
 }
 
 void describe(gemmepi_plan_s* p) {
@@ -196,13 +260,17 @@ void describe(gemmepi_plan_s* p) {
              (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
   } else {
     const TileCfg& c = kTiles[p->tile];
+    char split_buf[64] = "";
+    if (p->splits > 1)
+      snprintf(split_buf, sizeof(split_buf), " splits=%d kt_split=%d", p->splits, p->kt_split);
     snprintf(buf, sizeof(buf),
              "path=gemm M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x tile=%s tiles=%dx%d "
-             "raster=%s%s%s",
+             "raster=%s%s%s%s",
              (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
              epis[p->epi], p->flags, c.name, p->tiles_m, p->tiles_n,
              p->sb_m ? "chip16x16/xcd4x8" : (p->xcd_remap ? "xcd_remap,group8" : "group8"),
-             p->tuned ? " tuned" : "", (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
+             split_buf, p->tuned ? " tuned" : "",
+             (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
   }
   p->info = buf;
 }
@@ -270,7 +338,29 @@ GemmArgs gemm_args(const gemmepi_plan_s& p, const void* A, const void* B, void* 
   g.sb_n = p.sb_n;
   g.xcd_m = p.xcd_m;
   g.xcd_n = p.xcd_n;
+  g.splits = p.splits;
+  g.kt_split = p.kt_split;
   return g;
+}
+
+// Split-K layout of a tiled-GEMM plan (1 = none).
+void set_split(gemmepi_plan_s* p, int splits) {
+  split_shape(p->K, kTiles[p->tile].bk, splits, &p->splits, &p->kt_split);
+  if (p->splits <= 1) {
+    p->splits = 1;
+    p->kt_split = 0;
+  }
+}
+
+// Workspace of a split plan: the arrival counters (one per tile, padded to
+// 256 bytes), then one fp32 partial tile per (tile, split).
+size_t counter_bytes(const gemmepi_plan_s& p) {
+  return ((size_t)p.tiles_m * p.tiles_n * 4 + 255) / 256 * 256;
+}
+size_t workspace_bytes(const gemmepi_plan_s& p) {
+  if (p.path != PATH_GEMM || p.splits <= 1) return 0;
+  const TileCfg& c = kTiles[p.tile];
+  return counter_bytes(p) + (size_t)p.tiles_m * p.tiles_n * p.splits * c.bm * c.bn * 4;
 }
 
 // Tile, grid shape and raster of a tiled-GEMM plan.
@@ -299,7 +389,7 @@ void set_tile(gemmepi_plan_s* p, int tile) {
 
 gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
                            gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags,
-                           int32_t tile_req) {
+                           int32_t tile_req, int32_t splits_req) {
   if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "plan: null output pointer");
   *plan = nullptr;
   if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
@@ -312,6 +402,14 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
   if (flags & ~kAllFlags) return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown flag bits 0x%x", flags);
   if (tile_req < -1 || tile_req >= kNumTiles)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "unknown tile id %d", tile_req);
+  if (splits_req < -1 || splits_req > kMaxSplits)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "splits %d outside [0, %d]", splits_req, kMaxSplits);
+  const bool norm_epi = epi == GEMMEPI_EPI_BIAS_RES_RMSNORM || epi == GEMMEPI_EPI_BIAS_RES_LAYERNORM;
+  if (norm_epi && splits_req > 1)
+    return fail(GEMMEPI_ERR_UNSUPPORTED, "the norm epilogues do not split K");
+  // what plan() does about K splits: 1 never, 0 choose, > 1 as requested
+  int split_mode = splits_req >= 0 ? splits_req : ((flags & GEMMEPI_FLAG_SPLIT_K) ? 0 : 1);
+  if (norm_epi) split_mode = 1;
   const bool bt = flags & GEMMEPI_FLAG_B_TRANS;
   if (K % 8 != 0)
     return fail(GEMMEPI_ERR_MISALIGNED, "K=%lld must be a multiple of 8", (long long)K);
@@ -326,7 +424,7 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
   if (M * N > (int64_t)1 << 40)
     return fail(GEMMEPI_ERR_UNSUPPORTED, "output too large");
 
-  const Key key{M, N, K, (int)dtype, (int)epi, flags, tile_req};
+  const Key key{M, N, K, (int)dtype, (int)epi, flags, tile_req, splits_req};
   std::lock_guard<std::mutex> lock(g_mu);
   auto it = cache().find(key);
   if (it != cache().end()) {
@@ -343,27 +441,39 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
   p->epi = (int)epi;
   p->flags = flags;
   p->tile_req = tile_req;
+  p->splits_req = splits_req;
+  p->splits = 1;
   p->refs = 1;
   const bool decode_epi = epi == GEMMEPI_EPI_DEFAULT || epi == GEMMEPI_EPI_BIAS ||
                           epi == GEMMEPI_EPI_RELU_BIAS || epi == GEMMEPI_EPI_GELU_BIAS;
-  if (tile_req < 0 && !(flags & GEMMEPI_FLAG_NO_DECODE) && bt && M <= 16 && decode_epi) {
+  if (tile_req < 0 && split_mode <= 1 && !(flags & GEMMEPI_FLAG_NO_DECODE) && bt && M <= 16 &&
+      decode_epi) {
     p->path = PATH_DECODE;
     p->tile = -1;
     const int64_t per = (K + 8 * 32 - 1) / (8 * 32) * 32;  // 8 waves, 32-wide steps
     p->k_per_wave = (int)per;
   } else {
     int tile = tile_req;
+    int splits = split_mode;
     if (tile < 0) {
       load_tune_cache();
       auto t = tuned().find(TuneKey{M, N, K, (int)dtype, (int)epi, flags});
       if (t != tuned().end()) {
         tile = t->second;
         p->tuned = 1;
-      } else {
-        tile = choose_tile(M, N, K);
+        if (splits == 0) splits = 1;
       }
     }
+    if (splits == 0)
+      choose_split(M, N, K, &tile, &splits);  // keeps an explicit tile
+    else if (tile < 0)
+      tile = choose_tile(M, N, K);
     set_tile(p, tile);
+    set_split(p, splits);
+    if ((int64_t)p->tiles_m * p->tiles_n * p->splits > 0x7FFFFFFFLL) {
+      delete p;
+      return fail(GEMMEPI_ERR_UNSUPPORTED, "grid too large");
+    }
   }
   describe(p);
   if (log_enabled()) fprintf(stderr, "[gemmepi] plan %s\n", p->info.c_str());
@@ -379,7 +489,7 @@ bool plan_live(gemmepi_plan_t plan) {
 }
 
 gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void* B, void* bias,
-                              void* aux, void* out, void* stream) {
+                              void* aux, void* out, void* ws, size_t ws_bytes, void* stream) {
   const int epi = p.epi;
   const bool bt = p.flags & GEMMEPI_FLAG_B_TRANS;
   const bool per_col = p.flags & GEMMEPI_FLAG_BIAS_PER_COL;
@@ -402,6 +512,18 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
     return fail(GEMMEPI_ERR_MISALIGNED, "execute: bias misaligned");
   if (needs_aux && !aligned(aux, 16))
     return fail(GEMMEPI_ERR_MISALIGNED, "execute: aux must be 16-byte aligned");
+  const size_t ws_need = workspace_bytes(p);
+  if (ws_need > 0) {
+    if (!ws)
+      return fail(GEMMEPI_ERR_INVALID_VALUE,
+                  "execute: the plan splits K and needs a workspace of %zu bytes "
+                  "(gemmepi_execute_ws)", ws_need);
+    if (ws_bytes < ws_need)
+      return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: workspace of %zu bytes, the plan needs %zu",
+                  ws_bytes, ws_need);
+    if (!aligned(ws, 256))
+      return fail(GEMMEPI_ERR_MISALIGNED, "execute: workspace must be 256-byte aligned");
+  }
 
   gemmepi_status_t st = check_device();
   if (st != GEMMEPI_OK) return st;
@@ -411,6 +533,7 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
     if ((st = check_device_ptr(out, "out")) != GEMMEPI_OK) return st;
     if (needs_bias && (st = check_device_ptr(bias, "bias")) != GEMMEPI_OK) return st;
     if (needs_aux && (st = check_device_ptr(aux, "aux")) != GEMMEPI_OK) return st;
+    if (ws_need > 0 && (st = check_device_ptr(ws, "workspace")) != GEMMEPI_OK) return st;
   }
 
   hipStream_t s = (hipStream_t)stream;
@@ -450,6 +573,10 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
     g.aux_ld = aux_ld;
     g.epi = core_epi;
     g.bias_per_col = per_col ? 1 : 0;
+    if (ws_need > 0) {
+      g.counters = (uint32_t*)ws;
+      g.ws = (float*)((uint8_t*)ws + counter_bytes(p));
+    }
     e = launch_gemm(p.dtype, bt, p.tile, g, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
   }
@@ -484,13 +611,33 @@ extern "C" {
 
 gemmepi_status_t gemmepi_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
                               gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags) {
-  return make_plan(plan, M, N, K, dtype, epi, flags, -1);
+  return make_plan(plan, M, N, K, dtype, epi, flags, -1, -1);
 }
 
 gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
                                     gemmepi_dtype_t dtype, gemmepi_epilogue_t epi,
                                     uint32_t flags, int32_t tile_id) {
-  return make_plan(plan, M, N, K, dtype, epi, flags, tile_id);
+  return make_plan(plan, M, N, K, dtype, epi, flags, tile_id, -1);
+}
+
+gemmepi_status_t gemmepi_plan_split(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
+                                    gemmepi_dtype_t dtype, gemmepi_epilogue_t epi,
+                                    uint32_t flags, int32_t tile_id, int32_t splits) {
+  if (splits < 0)
+    return fail(GEMMEPI_ERR_INVALID_VALUE, "splits %d outside [0, %d]", splits, kMaxSplits);
+  return make_plan(plan, M, N, K, dtype, epi, flags, tile_id, splits);
+}
+
+size_t gemmepi_workspace_bytes(gemmepi_plan_t plan) {
+  if (!plan) return 0;
+  return workspace_bytes(*plan);
+}
+
+gemmepi_status_t gemmepi_execute_ws(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
+                                    void* aux, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: null plan");
+  return execute_impl(*plan, A, B, bias, aux, out, workspace, workspace_bytes, stream);
 }
 
 gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const void* B,
@@ -635,7 +782,7 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
   if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: null plan");
   // The plan is immutable after creation (autotune excepted); callers keep
   // it alive while they execute it, so no lock is taken on this path.
-  return execute_impl(*plan, A, B, bias, aux, out, stream);
+  return execute_impl(*plan, A, B, bias, aux, out, nullptr, 0, stream);
 }
 
 gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
@@ -650,6 +797,8 @@ gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void
     return fail(GEMMEPI_ERR_UNSUPPORTED, "autotune: norm plans are not tuned");
   if (p.tile_req >= 0)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "autotune: the plan has an explicit tile");
+  if (p.splits > 1)
+    return fail(GEMMEPI_ERR_UNSUPPORTED, "autotune: split-K plans are not tuned");
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
@@ -662,11 +811,11 @@ gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void
   for (int t = 0; t < kNumTiles && st == GEMMEPI_OK; ++t) {
     gemmepi_plan_s q = p;  // same operands, another tile
     set_tile(&q, t);
-    st = execute_impl(q, A, B, bias, aux, out, stream);  // warm-up (validates the arguments)
+    st = execute_impl(q, A, B, bias, aux, out, nullptr, 0, stream);  // warm-up (validates the arguments)
     if (st != GEMMEPI_OK) break;
     hipError_t e = hipEventRecord(e0, s);
     for (int r = 0; r < reps && st == GEMMEPI_OK; ++r)
-      st = execute_impl(q, A, B, bias, aux, out, stream);
+      st = execute_impl(q, A, B, bias, aux, out, nullptr, 0, stream);
     if (st != GEMMEPI_OK) break;
     if (e == hipSuccess) e = hipEventRecord(e1, s);
     if (e == hipSuccess) e = hipEventSynchronize(e1);

@@ -52,6 +52,13 @@ struct GemmArgs {
   // sb_m x sb_n tiles, one tile per CU; XCD x owns the sub-block
   // (x / xcd_n, x % xcd_n) of (sb_m / xcd_m) x (sb_n / xcd_n) tiles.
   int sb_m, sb_n, xcd_m, xcd_n;
+  // split-K (splits > 1): workgroup split * tiles + t runs k slabs
+  // [split * kt_split, min(KT, (split + 1) * kt_split)) of tile t and writes
+  // its fp32 partial tile to ws; the last of the tile's splits to arrive
+  // (counters) sums the partials in split order and runs the epilogue
+  int splits, kt_split;
+  float* ws;           // [tiles][splits][BM * BN] fp32 partial tiles
+  uint32_t* counters;  // [tiles] arrival counts; zero before and after a launch
 };
 
 // Arguments of the thin-M decode kernel.
@@ -73,7 +80,7 @@ struct TileCfg {
   const char* name;
 };
 
-constexpr int kNumTiles = 9;
+constexpr int kNumTiles = 8;
 extern const TileCfg kTiles[kNumTiles];
 
 // Launchers (defined in the per-dtype/per-layout instantiation files).

@@ -104,7 +104,11 @@ class Workload:
                 self.aux = torch.empty(c.M, ge.aux_ld_words(c.N), dtype=torch.int32, device=dev)
             if c.epilogue == "GELU_AUX_BIAS":
                 self.aux = torch.empty(c.M, c.N, dtype=tdt, device=dev)
-        f = flags | (ge.FLAG_B_TRANS if c.b_trans else 0) | (ge.FLAG_BIAS_PER_COL if c.bias_per_col else 0)
+        # FLAG_SPLIT_K: plan() may split K for the wave-quantised shapes (C0,
+        # the 512-token down-projection); its workspace is allocated by the
+        # plan at the first (warm-up) execution
+        f = flags | ge.FLAG_SPLIT_K | (ge.FLAG_B_TRANS if c.b_trans else 0) | \
+            (ge.FLAG_BIAS_PER_COL if c.bias_per_col else 0)
         self.fused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f)
         self.unfused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f | ge.FLAG_UNFUSED)
         self.flops = 2.0 * c.M * c.N * c.K

@@ -104,7 +104,13 @@ enum {
    * addition ...", paragraph 5). Costs a few host calls. */
   GEMMEPI_FLAG_VALIDATE = 1u << 3,
   /* Never use the thin-M decode kernel; always use the tiled MFMA GEMM. */
-  GEMMEPI_FLAG_NO_DECODE = 1u << 4
+  GEMMEPI_FLAG_NO_DECODE = 1u << 4,
+  /* Let plan() split K over several workgroups per output tile (split-K)
+   * when the shape has too few output tiles to fill the 256 CUs.  Such a
+   * plan needs a device workspace (gemmepi_workspace_bytes) and runs
+   * through gemmepi_execute_ws.  No effect on the decode kernel and the
+   * norm epilogues. */
+  GEMMEPI_FLAG_SPLIT_K = 1u << 5
 };
 
 /* Opaque, reference-counted handle to a cached plan. */
@@ -144,6 +150,34 @@ gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, 
                                     uint32_t flags, int32_t tile_id);
 
 /*
+ * As gemmepi_plan_tiled, with an explicit K split (split-K): the k slabs of
+ * each output tile are divided into `splits` contiguous ranges, each run by
+ * its own workgroup; every range writes an fp32 partial tile to the
+ * workspace, and the last range of a tile to finish sums the partials in
+ * range order (so out does not depend on which finishes last) and applies
+ * the epilogue once.  This is the wave-quantisation remedy for shapes with
+ * few output tiles and a long K.
+ *
+ *   splits  1 = no split; 2 .. 64 = that many ranges (fewer when K has
+ *           fewer k slabs of the tile); 0 = chosen by plan() with the tile
+ *           (as GEMMEPI_FLAG_SPLIT_K)
+ *   tile_id -1 = chosen; an explicit tile or splits > 1 disables the
+ *           decode kernel
+ * Errors: as gemmepi_plan_tiled, plus INVALID_VALUE for splits outside
+ * [0, 64], UNSUPPORTED for splits > 1 with a norm epilogue.
+ */
+gemmepi_status_t gemmepi_plan_split(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
+                                    gemmepi_dtype_t dtype, gemmepi_epilogue_t epi,
+                                    uint32_t flags, int32_t tile_id, int32_t splits);
+
+/*
+ * Device workspace a plan needs, in bytes: 0 unless the plan splits K.
+ * Then it is 4 bytes per output tile (arrival counters, padded to 256
+ * bytes) plus one fp32 partial tile per (tile, split).  NULL plan: 0.
+ */
+size_t gemmepi_workspace_bytes(gemmepi_plan_t plan);
+
+/*
  * Enqueue one execution on `stream` (a hipStream_t; NULL = the null
  * stream) and return without synchronising.  No allocation, no host sync.
  *
@@ -176,7 +210,34 @@ gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, 
 gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
                                  void* aux, void* out, void* stream);
 /* (A plan with a norm epilogue is rejected by gemmepi_execute with
- * INVALID_VALUE; it runs through gemmepi_execute_norm below.) */
+ * INVALID_VALUE; it runs through gemmepi_execute_norm below.  A plan that
+ * splits K is rejected too: it runs through gemmepi_execute_ws.) */
+
+/*
+ * gemmepi_execute with a caller-owned device workspace, which a plan that
+ * splits K needs (gemmepi_workspace_bytes > 0); the vendor library's matmul
+ * likewise takes its workspace from the caller ("Bias fusion with cuBLASLt
+ * in PyTorch inference", body).  For a plan that does not split K it is
+ * identical to gemmepi_execute and the workspace is ignored.
+ *
+ *   workspace        device memory, 256-byte aligned, at least
+ *                    gemmepi_workspace_bytes(plan) bytes.  Its counter
+ *                    area must be zero before its first use: zero the whole
+ *                    workspace once after allocating it.  Every execution
+ *                    leaves the counters at zero again, so a workspace can
+ *                    be reused by later executions of any plan on the same
+ *                    stream; executions that may overlap (other streams)
+ *                    need workspaces of their own.
+ *   workspace_bytes  its size
+ * The partial tiles are summed in split order, so out and aux stay bitwise
+ * reproducible.
+ * Errors: as gemmepi_execute, plus INVALID_VALUE (workspace missing or too
+ * small), MISALIGNED (workspace), DEVICE (VALIDATE: workspace not device
+ * memory of the current device).
+ */
+gemmepi_status_t gemmepi_execute_ws(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
+                                    void* aux, void* out, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * Measured tile choice for a tiled-GEMM plan: the pages' planner "tries
@@ -196,7 +257,7 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
  *            milliseconds per execution
  * Not thread-safe against executions of the same plan on other threads.
  * Errors: INVALID_VALUE (null plan, reps, a plan made with an explicit
- * tile), UNSUPPORTED (decode or norm plans), the errors of
+ * tile), UNSUPPORTED (decode, norm or split-K plans), the errors of
  * gemmepi_execute, HIP (timing, or the cache file could not be written).
  */
 gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void* B, void* bias,

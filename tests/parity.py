@@ -66,7 +66,7 @@ class GpuRun:
     """Device buffers and results of one execution of a GemmCase."""
 
     def __init__(self, case, flags: int = 0, tile: int = -1, A_dev=None, guard: int = 0,
-                 device="cuda"):
+                 device="cuda", splits=None):
         import torch
         c = case
         self.case = c
@@ -112,7 +112,7 @@ class GpuRun:
                     self._zaux_full.view(torch.int16)[:guard] = GUARD_BITS
                     self._zaux_full.view(torch.int16)[-guard:] = GUARD_BITS
                 self.aux = self._zaux_full[guard:guard + M * N].view(M, N)
-        self.plan = ge.plan(M, N, K, c.dtype, c.epilogue, flags_of(c, flags), tile)
+        self.plan = ge.plan(M, N, K, c.dtype, c.epilogue, flags_of(c, flags), tile, splits)
         self.info = self.plan.info()
 
     def run(self, times: int = 1):

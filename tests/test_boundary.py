@@ -218,7 +218,7 @@ def test_autotune_validation_before_any_hip_call():
         assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, 4096, 4096, 3, None, None) == ge.ERR_UNSUPPORTED
     with ge.plan(512, 512, 512, "f16", "BIAS_RES_LAYERNORM", 0) as p:
         assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, 4096, 4096, 3, None, None) == ge.ERR_UNSUPPORTED
-    with ge.plan(512, 512, 512, "f16", "BIAS", 0, tile=3) as p:
+    with ge.plan(512, 512, 512, "f16", "BIAS", 0, tile=2) as p:
         assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, 4096, 4096, 3, None, None) == ge.ERR_INVALID_VALUE
 
 
@@ -228,7 +228,7 @@ def test_tune_cache_file_is_read_by_a_new_process(tmp_path):
     import subprocess
     import sys
     f = tmp_path / "tune.txt"
-    f.write_text("gemmepi-tune-v1 1000 1000 1000 0 1 0 5\n"      # f16 BIAS, no flags -> tile 5
+    f.write_text("gemmepi-tune-v1 1000 1000 1000 0 1 0 4\n"      # f16 BIAS, no flags -> tile 4
                  "garbage line\n"
                  "gemmepi-tune-v1 2000 2000 2000 0 1 0 99\n"     # tile out of range
                  "gemmepi-tune-v2 3000 3000 3000 0 1 0 4\n")     # unknown version
@@ -240,5 +240,72 @@ def test_tune_cache_file_is_read_by_a_new_process(tmp_path):
                        timeout=120)
     assert r.returncode == 0, r.stderr
     lines = r.stdout.strip().splitlines()
-    assert ge.tile_name(5) in lines[0] and "tuned" in lines[0]
+    assert ge.tile_name(4) in lines[0] and "tuned" in lines[0]
     assert "tuned" not in lines[1] and "tuned" not in lines[2]
+
+
+def _plan_split(M, N, K, epi=1, flags=0, tile=-1, splits=2):
+    lib = ge.library()
+    h = ctypes.c_void_p()
+    st = lib.gemmepi_plan_split(ctypes.byref(h), M, N, K, 0, epi, flags, tile, splits)
+    return st, h
+
+
+def test_split_plan_validation_and_workspace_size():
+    lib = ge.library()
+    for bad in (-1, 65):
+        st, _ = _plan_split(512, 512, 4096, splits=bad)
+        assert st == ge.ERR_INVALID_VALUE
+    st, _ = _plan_split(512, 512, 4096, epi=6, splits=2)        # norm epilogue
+    assert st == ge.ERR_UNSUPPORTED
+    # splits = 1 and unsplit plans need no workspace
+    with ge.plan(512, 512, 4096, "f16", "BIAS", 0, tile=3, splits=1) as p:
+        assert p.workspace_bytes() == 0 and "splits=" not in p.info()
+    with ge.plan(512, 512, 4096, "f16", "BIAS", 0) as p:
+        assert p.workspace_bytes() == 0
+    assert lib.gemmepi_workspace_bytes(None) == 0
+    # 128x128 tiles: 4 x 4 tiles, K = 4096 -> 64 slabs; 3 splits of 22, 22, 20
+    with ge.plan(512, 512, 4096, "f16", "BIAS", 0, tile=3, splits=3) as p:
+        assert "splits=3 kt_split=22" in p.info(), p.info()
+        assert p.workspace_bytes() == 256 + 16 * 3 * 128 * 128 * 4
+    # more splits than k slabs: one slab per range
+    with ge.plan(64, 64, 72, "f16", "BIAS", 0, tile=5, splits=64) as p:
+        assert "splits=2 kt_split=1" in p.info(), p.info()
+    # a split request disables the decode kernel; the norms ignore the flag
+    with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", ge.FLAG_B_TRANS | ge.FLAG_BIAS_PER_COL,
+                 splits=2) as p:
+        assert "path=gemm" in p.info()
+    with ge.plan(512, 512, 4096, "f16", "BIAS_RES_RMSNORM", ge.FLAG_SPLIT_K) as p:
+        assert "splits=" not in p.info()
+
+
+def test_split_flag_chooses_only_for_wave_quantised_shapes():
+    def info(M, N, K, bt):
+        f = ge.FLAG_SPLIT_K | (ge.FLAG_B_TRANS if bt else 0)
+        with ge.plan(M, N, K, "f16", "BIAS", f) as p:
+            return p.info(), p.workspace_bytes()
+    i, ws = info(512, 4096, 11008, True)       # 512-token FFN down-projection
+    assert "splits=" in i and ws > 0, i
+    for M, N, K, bt in ((65536, 8192, 16384, False), (2048, 4096, 11008, True),
+                        (4096, 4096, 4096, True)):
+        i, ws = info(M, N, K, bt)
+        assert "splits=" not in i and ws == 0, i
+
+
+def test_split_execute_validation():
+    lib = ge.library()
+    with ge.plan(512, 512, 4096, "f16", "BIAS", 0, tile=3, splits=2) as p:
+        need = p.workspace_bytes()
+        # gemmepi_execute refuses a plan that needs a workspace
+        assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, None, 4096, None) == ge.ERR_INVALID_VALUE
+        assert "workspace" in ge.last_error()
+        ex = lib.gemmepi_execute_ws
+        assert ex(p._h, 4096, 4096, 4096, None, 4096, None, need, None) == ge.ERR_INVALID_VALUE
+        assert ex(p._h, 4096, 4096, 4096, None, 4096, 1 << 20, need - 1, None) == \
+            ge.ERR_INVALID_VALUE
+        assert ex(p._h, 4096, 4096, 4096, None, 4096, (1 << 20) + 16, need, None) == \
+            ge.ERR_MISALIGNED
+    with ge.plan(512, 512, 4096, "f16", "BIAS", 0, splits=2) as p:
+        assert "splits=2" in p.info()
+        assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, None, 4096, 3, None, None) == \
+            ge.ERR_UNSUPPORTED

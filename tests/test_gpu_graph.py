@@ -4,7 +4,8 @@ synchronisations in between, must match an eager execution of the same
 plan bit for bit.  Integer inputs make every fp32 sum exact, so this holds
 for the bias gradient too, whatever the order of its atomic additions.
 DRELU_BGRAD exercises the zero-fill kernel that precedes the GEMM (a fill
-kernel, not a memset node, so that replays re-zero the gradient)."""
+kernel, not a memset node, so that replays re-zero the gradient).  Split-K
+plans capture the workspace their Plan allocated at the warm-up."""
 import numpy as np
 import pytest
 
@@ -28,19 +29,23 @@ def _buffers(c):
     return d
 
 
-@pytest.mark.parametrize("epi,b_trans,tile", [
-    ("RELU_AUX_BIAS", False, -1),
-    ("DRELU_BGRAD", False, -1),
-    ("GELU_BIAS", True, 7),
-    ("BIAS", True, 8),
+@pytest.mark.parametrize("epi,b_trans,tile,splits", [
+    ("RELU_AUX_BIAS", False, -1, None),
+    ("DRELU_BGRAD", False, -1, None),
+    ("GELU_BIAS", True, 6, None),
+    ("BIAS", True, 7, None),
+    # split-K: the arrival counters must be back at zero for every replay
+    ("RELU_AUX_BIAS", False, 3, 3),
+    ("DRELU_BGRAD", True, 5, 2),
 ])
-def test_graph_replays_match_eager(epi, b_trans, tile):
+def test_graph_replays_match_eager(epi, b_trans, tile, splits):
     import torch
     M, N, K = 520, 392, 264
     cases = [wl.random_case(M, N, K, "f16", epi, b_trans, b_trans, 4000 + 17 * r, kind="int")
              for r in range(4)]
     flags = flags_of(cases[0])
-    with ge.plan(M, N, K, "f16", epi, flags, tile=tile) as p:
+    with ge.plan(M, N, K, "f16", epi, flags, tile=tile, splits=splits) as p:
+        assert (p.workspace_bytes() > 0) == (splits is not None)
         cap = _buffers(cases[0])
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())

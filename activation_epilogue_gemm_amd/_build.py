@@ -46,7 +46,7 @@ def common_flags(extra=()):
         "-O3",
         "-std=c++17",
         "-fPIC",
-        # packed fp32 VALU ops are not generated (see the design notes)
+        # keep fp32 arithmetic scalar: no packed fp32 VALU instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
         f"-I{INCLUDE}", f"-I{CSRC}",

@@ -537,7 +537,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     });
     wait_vmcnt<0>();  // this thread's slot stores are complete
     __syncthreads();  // ... and every thread's
-    __shared__ uint32_t s_last;
+    // the flag lives in the (drained) staging ring: a separate LDS variable
+    // would push the largest rings past the 160 KiB of a CU
+    uint32_t& s_last = *(uint32_t*)smem;
     if (tid == 0) {
       const uint32_t before = __hip_atomic_fetch_add(&p.counters[tile_id], 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
@@ -546,7 +548,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       s_last = last;
     }
     __syncthreads();
-    if (s_last == 0u) return;  // uniform over the workgroup
+    const uint32_t is_last = s_last;
+    __syncthreads();  // every thread has read the flag before the epilogue reuses the ring
+    if (is_last == 0u) return;  // uniform over the workgroup
     // one slot per pass, in steps of 16 or 32 independent loads (hoisting
     // all loads of a slot would spill the accumulators)
     constexpr int FNG = FN > 2 ? 1 : FN;  // accumulator blocks per step

@@ -36,7 +36,7 @@ with these epilogues (the MatmulEpilog members the pages name):
                  dZ = acc * gelu'(z) with z the stored pre-activation and
                  gelu'(z) = Phi(z) + z phi(z); bgrad[j] = sum_i dZ[i,j]
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
   * accumulate in fp32 on the device, fp64 here; alpha = 1, beta = 0;
   * ReLU keeps z only when z > 0; the mask bit is (z > 0) on the unrounded z;
   * the bias is converted to the accumulator type and added before one

@@ -40,6 +40,13 @@ const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 //   est = rounds * min(occ, ceil(tiles / kNumCU)) * BM * BN / eff.
 static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95};
 static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 2, 3, 1, 1};
+// With B stored [N,K] both operands are K-contiguous; a 32-wide k slab then
+// fetches 64-byte row segments of both, which measured 0.83x on the
+// 65536 x 8192 x 16384 shape (64-wide slabs fetch whole 128-byte lines and
+// lose nothing).
+double tile_eff(int t, bool bt) {
+  return kTileEff[t] * ((bt && kTiles[t].bk < 64) ? 0.83 : 1.0);
+}
 constexpr int kNumCU = 256;
 
 hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s) {
@@ -186,7 +193,7 @@ void split_shape(int64_t K, int bk, int splits, int* eff_splits, int* kt_split) 
 // MFMA work (BM * BN * k) over the tile's efficiency, plus, when K is
 // split, the partial-tile round trip (all splits' partials are read by the
 // last one: kSplitCost * BM * BN * splits).
-double tile_estimate(int t, int64_t M, int64_t N, int64_t K, int splits) {
+double tile_estimate(int t, int64_t M, int64_t N, int64_t K, bool bt, int splits) {
   const TileCfg& c = kTiles[t];
   int s = 1, per = 0;
   split_shape(K, c.bk, splits, &s, &per);
@@ -195,16 +202,16 @@ double tile_estimate(int t, int64_t M, int64_t N, int64_t K, int splits) {
   const int64_t rounds = (units + slots - 1) / slots;
   const int64_t per_cu = (units + kNumCU - 1) / kNumCU;
   const int64_t share = per_cu < kTileOcc[t] ? per_cu : kTileOcc[t];
-  double unit = (double)c.bm * c.bn * per * c.bk / kTileEff[t];
+  double unit = (double)c.bm * c.bn * per * c.bk / tile_eff(t, bt);
   if (s > 1) unit += kSplitCost * c.bm * c.bn * s;
   return (double)rounds * share * unit;
 }
 
-int choose_tile(int64_t M, int64_t N, int64_t K) {
+int choose_tile(int64_t M, int64_t N, int64_t K, bool bt) {
   int best = 0;
   double best_est = 0.0;
   for (int t = 0; t < kNumTiles; ++t) {
-    const double est = tile_estimate(t, M, N, K, 1);
+    const double est = tile_estimate(t, M, N, K, bt, 1);
     if (t == 0 || est < best_est) {
       best = t;
       best_est = est;
@@ -216,19 +223,19 @@ int choose_tile(int64_t M, int64_t N, int64_t K) {
 // Tile (when tile < 0) and split count for a split-K-enabled plan: the
 // best unsplit estimate, unless some split count in {2, 3, 4, 6, 8, 16}
 // is estimated kSplitGain faster.
-void choose_split(int64_t M, int64_t N, int64_t K, int* tile, int* splits) {
+void choose_split(int64_t M, int64_t N, int64_t K, bool bt, int* tile, int* splits) {
   const int t0 = *tile < 0 ? 0 : *tile, t1 = *tile < 0 ? kNumTiles : *tile + 1;
   static const int kCand[] = {2, 3, 4, 6, 8, 16};
-  int bt = t0, bst = t0, bss = 1;
+  int b1 = t0, bst = t0, bss = 1;
   double best1 = 0.0, bests = 0.0;
   for (int t = t0; t < t1; ++t) {
-    const double e1 = tile_estimate(t, M, N, K, 1);
+    const double e1 = tile_estimate(t, M, N, K, bt, 1);
     if (t == t0 || e1 < best1) {
       best1 = e1;
-      bt = t;
+      b1 = t;
     }
     for (int s : kCand) {
-      const double es = tile_estimate(t, M, N, K, s);
+      const double es = tile_estimate(t, M, N, K, bt, s);
       if (bests == 0.0 || es < bests) {
         bests = es;
         bst = t;
@@ -240,7 +247,7 @@ void choose_split(int64_t M, int64_t N, int64_t K, int* tile, int* splits) {
     *tile = bst;
     *splits = bss;
   } else {
-    *tile = bt;
+    *tile = b1;
     *splits = 1;
   }
 }
@@ -465,9 +472,9 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
       }
     }
     if (splits == 0)
-      choose_split(M, N, K, &tile, &splits);  // keeps an explicit tile
+      choose_split(M, N, K, bt, &tile, &splits);  // keeps an explicit tile
     else if (tile < 0)
-      tile = choose_tile(M, N, K);
+      tile = choose_tile(M, N, K, bt);
     set_tile(p, tile);
     set_split(p, splits);
     if ((int64_t)p->tiles_m * p->tiles_n * p->splits > 0x7FFFFFFFLL) {

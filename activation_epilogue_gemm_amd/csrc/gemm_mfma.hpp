@@ -273,7 +273,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   constexpr int NT = G::NT, NW = G::NW, WTM = G::WTM, WTN = G::WTN, FM = G::FM, FN = G::FN;
   constexpr int KCH = G::KCH, NCH = G::NCH, A_CH = G::A_CH, B_CH = G::B_CH;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[G::SMEM];
+  // schedule 2 keeps A in a ring of 3 double-wide slabs and B in a ring of
+  // NS slabs
+  constexpr int RING2 = 3 * BM * (2 * BK) * 2 + NS * G::B_BYTES;
+  constexpr int SMEM_BYTES = (SCHED == 2 && RING2 > G::SMEM) ? RING2 : G::SMEM;
+  static_assert(SMEM_BYTES <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -441,6 +446,119 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     }
   };
 
+  if constexpr (SCHED == 2) {
+    // Ping-pong (as schedule 1) with A fetched in double-wide slabs.  A is
+    // K-contiguous, and a 32-wide slab gives each load instruction 16 rows x
+    // 64 bytes, half a 128-byte line per row; a 64-wide A slab gives 8 rows
+    // x 128 bytes.  A lives in a ring of 3 double slabs (pair q = slabs 2q,
+    // 2q + 1 of the range), B in a ring of 4 slabs, 160 KiB together.  The
+    // compute phase of slab i issues B slab i + 3 and, after an odd slab, A
+    // pair (i + 3) / 2, so a load phase may leave in flight exactly the
+    // loads of the previous compute phase: B's, plus A's after an odd slab.
+    static_assert(SCHED != 2 || NS == 4, "schedule 2 issues B three slabs ahead");
+    constexpr int BK2 = 2 * BK, KCH2 = BK2 / 8, RPB2 = 1024 / (BK2 * 2);
+    constexpr int RPK2 = (BK2 * 2 >= 256) ? 1 : 256 / (BK2 * 2);
+    constexpr int A2_BYTES = BM * BK2 * 2;
+    constexpr int A2_CH = A2_BYTES / (NT * 16);  // A loads per wave per pair
+    constexpr int NA = 3;
+    static_assert(A2_BYTES % (NT * 16) == 0 && 64 % KCH2 == 0, "load split");
+    static_assert((32 / RPK2) % KCH2 == 0, "A swizzle must repeat every 32 rows");
+    static_assert(A2_CH + G::B_CH <= FM * FN * KS, "one load after each MFMA");
+    auto swz2 = [](int r) { return (r / RPK2) % KCH2; };
+    uint8_t* const a_ring = smem;
+    uint8_t* const b_ring = smem + NA * A2_BYTES;
+    uint32_t a2_off[A2_CH];
+    int a2_k[A2_CH];
+#pragma unroll
+    for (int i = 0; i < A2_CH; ++i) {
+      const int blk = i * NW + wave;
+      const int r = blk * RPB2 + lane / KCH2;
+      const int kc = (lane % KCH2) ^ swz2(r);
+      a2_off[i] = (m0 + r < M) ? (uint32_t)((r * p.lda + kc * 8) * 2) : kOOB;
+      a2_k[i] = kc * 8;
+    }
+    const int k_stop = min(K, kt_end * BK);  // A columns at or past it read zero
+    auto issue_a2 = [&](int q, int stage, int j) {
+      const int slab0 = kt_begin + 2 * q;
+      const bool none = slab0 >= kt_end;
+      const int k0 = none ? 0 : slab0 * BK;
+      const uint32_t st_addr =
+          __builtin_amdgcn_readfirstlane(lds_addr_of(a_ring + stage * A2_BYTES));
+      const uint32_t kill = (none || k0 + a2_k[j] >= k_stop) ? kOOB : 0u;
+      const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (size_t)k0 * 2);
+      buffer_load16_lds(rA, st_addr + (j * NW + wave) * 1024, a2_off[j] | kill);
+    };
+    // B slab kt into B stage `stage` through the schedule-1 loader (its B
+    // offsets are relative to a stage whose A part is A_BYTES long)
+    auto issue_b2 = [&](int kt, int stage, int j) {
+      issue_one(kt, b_ring + stage * G::B_BYTES - G::A_BYTES, G::A_CH + j);
+    };
+    uint32_t a2_lds[2][KS];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = wm * WTM + lrow;
+        const int chunk = h * (BK / 8) + ks * 2 + khalf;
+        a2_lds[h][ks] = (uint32_t)(r * BK2 * 2 + ((chunk ^ swz2(r)) << 4));
+      }
+    // prologue, in this order (the waits count on it): A pair 0, B slabs 0
+    // and 1, A pair 1, B slab 2; then wait for slab 0
+#pragma unroll
+    for (int j = 0; j < A2_CH; ++j) issue_a2(0, 0, j);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + s2, s2, j);
+#pragma unroll
+    for (int j = 0; j < A2_CH; ++j) issue_a2(1, 1, j);
+#pragma unroll
+    for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + 2, 2, j);
+    wait_vmcnt<G::B_CH + A2_CH + G::B_CH>();
+    __syncthreads();
+    const int grp = wave >> 2;
+    if (grp == 1) phase_barrier();
+    const int npairs = (kt_end - kt_begin + 1) / 2;  // an odd range ends in a zero slab
+    int a_cur = 0;                                   // A stage of pair q
+    for (int q = 0; q < npairs; ++q) {
+      static_for<2>([&](auto h_c) {
+        constexpr int h = decltype(h_c)::value;
+        const int i = 2 * q + h;  // slab index in the range
+        const uint8_t* sa = a_ring + a_cur * A2_BYTES;
+        const uint8_t* sb = b_ring + (i & 3) * G::B_BYTES - G::A_BYTES;
+        V8 af[KS][FM], bf[KS][FN];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm)
+            af[ks][fm] = *(const V8*)(sa + a2_lds[h][ks] + fm * 32 * BK2 * 2);
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) bf[ks][fn] = read_b(sb, ks, fn);
+        }
+        wait_vmcnt<(h == 0) ? A2_CH + G::B_CH : G::B_CH>();
+        phase_barrier();
+        const int a_next = (a_cur + 2 >= NA) ? a_cur + 2 - NA : a_cur + 2;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          mfma_step(af[ks], bf[ks], [&](int qq) {
+            const int d = ks * FM * FN + qq;
+            if constexpr (h == 1) {
+              if (d < A2_CH)
+                issue_a2(q + 2, a_next, d);
+              else if (d < A2_CH + G::B_CH)
+                issue_b2(kt_begin + i + 3, (i + 3) & 3, d - A2_CH);
+            } else {
+              if (d < G::B_CH) issue_b2(kt_begin + i + 3, (i + 3) & 3, d);
+            }
+          });
+        phase_barrier();
+      });
+      a_cur = (a_cur + 1 == NA) ? 0 : a_cur + 1;
+    }
+    if (grp == 0) phase_barrier();
+    wait_vmcnt<0>();
+    __syncthreads();
+  } else {
   // prologue: the first NS-1 slabs (or placeholders) in flight, wait for the first
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) issue(kt_begin + s, smem + s * G::STAGE);
@@ -509,6 +627,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     cur = (cur + 1 == NS) ? 0 : cur + 1;
     nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
   }
+  }  // schedules 0 and 1
 
   // ---- split-K: partial tiles through the workspace ---------------------------
   // Each split writes its fp32 accumulators to its slot, element-major
@@ -873,8 +992,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 
 template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT, int SCHED>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
-  static_assert(SCHED == 0 || SCHED == 1, "schedule");
-  static_assert(SCHED != 1 || WM * WN == 8, "ping-pong pairs waves w and w + 4 on each SIMD");
+  static_assert(SCHED >= 0 && SCHED <= 2, "schedule");
+  static_assert(SCHED == 0 || WM * WN == 8, "ping-pong pairs waves w and w + 4 on each SIMD");
   static_assert(SCHED != 1 || NS >= 3, "ping-pong issues each slab NS - 1 ahead from a compute phase");
   static_assert(SCHED != 1 || (BK / 16) * (BM / WM / 32) * (BN / WN / 32) >=
                                   GemmTile<BM, BN, BK, WM, WN, NS>::LPS,

@@ -7,7 +7,10 @@
 // schedule 1: ping-pong -- the two wave rows alternate between a phase that
 // only loads (LDS -> registers, next slabs -> LDS) and a phase that only
 // issues MFMAs, so each SIMD always has one wave feeding its matrix core
-// (eight waves).
+// (eight waves);
+// schedule 2: ping-pong with A (K-contiguous) fetched in double-wide slabs,
+// so every A load instruction reads whole 128-byte lines: A in a ring of 3
+// double slabs, B in a ring of `stages` slabs (160 KiB for 256 x 256 x 32).
 #pragma once
 
 #define GEMMEPI_TILES(X)         \
@@ -18,4 +21,5 @@
   X(4, 128, 64, 64, 2, 2, 3, 0)  \
   X(5, 64, 64, 64, 2, 2, 3, 0)   \
   X(6, 256, 256, 32, 2, 4, 4, 1) \
-  X(7, 256, 128, 64, 4, 2, 3, 1)
+  X(7, 256, 128, 64, 4, 2, 3, 1) \
+  X(8, 256, 256, 32, 2, 4, 4, 2)

@@ -38,14 +38,16 @@ const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 // kNumCU * occ tiles; in one round a CU holds up to `occ` tiles that share
 // its MFMA units, so
 //   est = rounds * min(occ, ceil(tiles / kNumCU)) * BM * BN / eff.
-static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95};
-static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 2, 3, 1, 1};
+static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95, 1.08};
+static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 2, 3, 1, 1, 1};
 // With B stored [N,K] both operands are K-contiguous; a 32-wide k slab then
 // fetches 64-byte row segments of both, which measured 0.83x on the
-// 65536 x 8192 x 16384 shape (64-wide slabs fetch whole 128-byte lines and
-// lose nothing).
+// 65536 x 8192 x 16384 shape.  64-wide slabs fetch whole 128-byte lines and
+// lose nothing; schedule 2, which fetches A in 64-wide slabs, loses 0.98x
+// (its B rows stay 64-byte segments).
 double tile_eff(int t, bool bt) {
-  return kTileEff[t] * ((bt && kTiles[t].bk < 64) ? 0.83 : 1.0);
+  if (!bt || kTiles[t].bk >= 64) return kTileEff[t];
+  return kTileEff[t] * (kTiles[t].sched == 2 ? 0.98 : 0.83);
 }
 constexpr int kNumCU = 256;
 

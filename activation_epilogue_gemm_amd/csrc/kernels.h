@@ -80,7 +80,7 @@ struct TileCfg {
   const char* name;
 };
 
-constexpr int kNumTiles = 8;
+constexpr int kNumTiles = 9;
 extern const TileCfg kTiles[kNumTiles];
 
 // Launchers (defined in the per-dtype/per-layout instantiation files).

@@ -16,7 +16,7 @@ def _ref(c, rows=None):
                        c.dtype, c.norm, c.b_trans, rows=rows)
 
 
-@pytest.mark.parametrize("tile", [-1, 0, 2, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [-1, 0, 2, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("norm", ["LAYERNORM", "RMSNORM"])
 @pytest.mark.parametrize("b_trans", [False, True])
 def test_norm_every_tile(tile, norm, b_trans):

@@ -76,7 +76,7 @@ def run_and_check(c, flags=0, tile=-1, exact=False, guard=0, label=""):
 
 
 # ---------------------------------------------------------------- every tile, exact
-NUM_TILES = 8
+NUM_TILES = 9
 
 
 def test_tile_count():

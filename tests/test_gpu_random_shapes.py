@@ -15,7 +15,7 @@ from parity import BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_out, check_
 pytestmark = pytest.mark.gpu
 
 EPIS = list(O.EPILOGUES)
-NUM_TILES = 8
+NUM_TILES = 9
 
 
 def _cases(n, seed):

@@ -19,7 +19,7 @@ from parity import BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check
 pytestmark = pytest.mark.gpu
 
 EPIS = list(O.EPILOGUES)
-NUM_TILES = 8
+NUM_TILES = 9
 
 
 def say(*a):
@@ -81,7 +81,7 @@ def test_integer_exact_every_tile_and_split(tile, b_trans):
             assert " splits=" in info, info
 
 
-@pytest.mark.parametrize("tile", [0, 2, 4, 6, 7])
+@pytest.mark.parametrize("tile", [0, 2, 4, 6, 7, 8])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_normal_inputs_every_epilogue(tile, dtype):
     for ei, epi in enumerate(EPIS):

@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--profile-traffic", action="store_true",
                     help="only run a plain 1 GiB copy (calibration) and the C3 fp16 fused kernel "
                          "twice each, for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--compare-blas", action="store_true",
+                    help="instead of the step: time the fused call, the library's plain GEMM "
+                         "(epilogue DEFAULT) and torch.matmul (ROCm's BLAS) on the suite's GEMM "
+                         "shapes, interleaved; one JSON line per shape")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only run the 1 GiB copy (calibration) and 16 decode calls each at "
                          "T = 1 and T = 16 over 16 rotated weight copies, for rocprofv3 --pmc runs")
@@ -372,8 +376,96 @@ def profile_decode():
         torch.cuda.empty_cache()
 
 
+def compare_blas(only, trials=5):
+    """Context for the roofline figures: the vendor BLAS on the same shapes.
+
+    Per GEMM shape of the suite (plus C3 with B stored [N, K], the layout in
+    which both operands are K-contiguous): the fused call, the library's plain
+    GEMM (epilogue DEFAULT: the rounded product, no bias) and torch.matmul on
+    the same device buffers (hipBLASLt on ROCm; a plain GEMM, no epilogue),
+    timed interleaved so that all three see the same clock.  Each figure is
+    the median of `trials` timings of back-to-back calls."""
+    import statistics
+    import torch
+    import activation_epilogue_gemm_amd as ge
+    import workloads as wl
+    sel = set(only.split(",")) if only else {"c0", "c2", "c3", "c4"}
+    def ffn(v, which):
+        up, down = wl.config2_ffn(v)
+        wu = Workload(f"c2_{v}_up", up)
+        if which == "up":
+            return wu
+        wu.run(False)  # the down-projection reads the up-projection's output
+        return Workload(f"c2_{v}_down", down, A_dev=wu.out)
+
+    specs = []  # (name, workload builder, store B as [N, K])
+    if "c0" in sel:
+        specs.append(("c0_bias", lambda: Workload("c0_bias", wl.config0_bias()), False))
+    if "c2" in sel:
+        for v in ("b1s2048", "b1s512"):
+            for which in ("up", "down"):
+                specs.append((f"c2_{v}_{which}", lambda v=v, which=which: ffn(v, which), False))
+    if "c3" in sel:
+        for dt in ("f16", "bf16"):
+            specs.append((f"c3_relu_aux_{dt}",
+                          lambda dt=dt: Workload("c3", wl.config3_relu_aux(dt)), False))
+        specs.append(("c3_relu_aux_f16_BNK",
+                      lambda: Workload("c3", wl.config3_relu_aux("f16")), True))
+    if "c4" in sel:
+        specs.append(("c4_drelu_bgrad", lambda: Workload("c4", wl.config4_drelu_bgrad()), False))
+    stream = torch.cuda.current_stream()
+    for name, make, transpose_b in specs:
+        w = make()
+        c = w.case
+        B, b_trans = w.B, c.b_trans
+        if transpose_b:  # the same product with B stored [N, K]
+            B, b_trans = w.B.t().contiguous(), True
+            flags = ge.FLAG_SPLIT_K | ge.FLAG_B_TRANS | (ge.FLAG_BIAS_PER_COL if c.bias_per_col else 0)
+            w.fused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, flags)
+            w.B = B
+        f = ge.FLAG_SPLIT_K | (ge.FLAG_B_TRANS if b_trans else 0)
+        plain = ge.plan(c.M, c.N, c.K, c.dtype, "DEFAULT", f)
+        scratch = torch.empty_like(w.out)
+        Bop = B.t() if b_trans else B
+        fns = {
+            "fused": lambda i: w.run(False, i),
+            "plain": lambda i: plain.execute(w.A, B, None, None, scratch, check=False),
+            "blas": lambda i: torch.matmul(w.A, Bop, out=scratch),
+        }
+        reps = max(3, min(200, int(2.0e12 / w.flops * 5)))
+        for fn in fns.values():
+            for i in range(2):
+                fn(i)
+        torch.cuda.synchronize()
+        res = {k: [] for k in fns}
+        for _ in range(trials):
+            for k, fn in fns.items():
+                res[k].append(time_region(fn, reps, stream))
+        med = {k: statistics.median(v) for k, v in res.items()}
+        rec = {"compare": name, "M": c.M, "N": c.N, "K": c.K, "dtype": c.dtype,
+               "b_layout": "[N,K]" if b_trans else "[K,N]", "epilogue": c.epilogue,
+               "plan": w.fused.info(), "plain_plan": plain.info()}
+        for k, ms in med.items():
+            rec[f"{k}_ms"] = round(ms, 5)
+            rec[f"{k}_tflops"] = round(w.flops / ms / 1e9, 1)
+        rec["plain_vs_blas"] = round(med["blas"] / med["plain"], 3)
+        rec["fused_vs_blas"] = round(med["blas"] / med["fused"], 3)
+        print(json.dumps(rec), flush=True)
+        log(f"{name}: fused {rec['fused_tflops']} plain {rec['plain_tflops']} "
+            f"blas {rec['blas_tflops']} TFLOP/s")
+        del w, plain, scratch, B, Bop, fns
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.compare_blas:
+        import torch
+        import activation_epilogue_gemm_amd as ge
+        ge.library()
+        torch.cuda.set_device(0)
+        compare_blas(args.only)
+        return
     if args.profile_traffic or args.profile_decode:
         import torch  # noqa: F401
         import activation_epilogue_gemm_amd as ge

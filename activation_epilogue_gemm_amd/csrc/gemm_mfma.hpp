@@ -172,7 +172,23 @@ __device__ __forceinline__ float one_plus_erf_scaled(float z) {  // 1 + erf(z / 
   const float q = poly * __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
   return z >= 0.0f ? 2.0f - q : q;
 }
-__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * one_plus_erf_scaled(z); }
+// gelu(z) itself, from the same formula with fewer operations.  With
+// h = Phi(-|z|) = erfc(|z| / sqrt 2) / 2:
+//   z >= 0: z Phi(z) = z - z h,   z < 0: z Phi(z) = z h = -|z| h,
+// so gelu(z) = max(z, 0) - |z| h.  h is 7.1.26's q / 2 (coefficients
+// halved), and with u = |z| sqrt(log2(e) / 2) the exponential is 2^(-u^2)
+// and p x = (p / sqrt(log2 e)) u: 11 VALU operations and two
+// transcendentals per element.
+__device__ __forceinline__ float gelu_erf(float z) {
+  const float u = fabsf(z) * 0.8493218002880191f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.2727374808792225f, u, 1.0f));
+  float poly = fmaf(0.5307027145f, t, -0.7265760135f);
+  poly = fmaf(poly, t, 0.7107068705f);
+  poly = fmaf(poly, t, -0.142248368f);
+  poly = fmaf(poly, t, 0.127414796f);
+  const float h = poly * t * __builtin_amdgcn_exp2f(-(u * u));
+  return fmaf(-fabsf(z), h, fmaxf(z, 0.0f));
+}
 
 // gelu'(z) = Phi(z) + z phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi), with Phi
 // from the same erf evaluation.
@@ -245,7 +261,8 @@ struct GemmTile {
   // ([WN][BM][2] fp64 partial row sums for the norm epilogue)
   static constexpr int OUT_BYTES = BM * BN * 2;
   static constexpr int RED_BYTES = WM * BN * 4 > BM * WN * 16 ? WM * BN * 4 : BM * WN * 16;
-  static constexpr int EPI_BYTES = OUT_BYTES + RED_BYTES;
+  static constexpr int BIAS_BYTES = (BM > BN ? BM : BN) * 4;  // the tile's bias slice, fp32
+  static constexpr int EPI_BYTES = OUT_BYTES + RED_BYTES + BIAS_BYTES;
   static constexpr int SMEM = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
   static_assert(SMEM <= 160 * 1024, "LDS");
   static_assert(NT % (BN / 8) == 0 && BM % (NT / (BN / 8)) == 0, "epilogue copy split");
@@ -709,6 +726,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   const int wcol0 = wn * WTN;
   uint8_t* const so = smem;                                  // [BM][BN] of T
   float* const red = (float*)(smem + G::OUT_BYTES);          // [WM][BN] fp32
+  float* const bsl = (float*)(smem + G::OUT_BYTES + G::RED_BYTES);  // bias slice, fp32
 
   auto stage = [&](int rl, int cl, const float (&y)[16]) {
     uint8_t* row = so + rl * (BN * 2) + (cl & 7) * 2;
@@ -825,8 +843,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // rounded y and y^2 are kept in fp64 (the norm's variance is formed from
     // them by subtraction).
     load_tile((const T*)p.residual);
+    {
+      const T* bias = (const T*)p.bias;  // per column; may be null
+      for (int i = tid; i < BN; i += NT)
+        bsl[i] = (bias != nullptr && n0 + i < N) ? to_f32(bias[n0 + i]) : 0.0f;
+    }
     __syncthreads();
-    const T* bias = (const T*)p.bias;
     double* red64 = (double*)(smem + G::OUT_BYTES);  // [WN][BM][2]
     static_for<FM>([&](auto fm_c) {
       constexpr int fm = decltype(fm_c)::value;
@@ -841,13 +863,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           const int c_loc = cl + 8 * g;
           uint8_t* at = staged4(rl, c_loc);
           const u32x2 rw = *(const u32x2*)at;
+          const f32x4 b4 = *(const f32x4*)(bsl + c_loc);
           float y[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int c = n0 + c_loc + e;
             const uint16_t rb = (uint16_t)(rw[e >> 1] >> (16 * (e & 1)));
-            const float b = (bias != nullptr && c < N) ? to_f32(bias[c]) : 0.0f;
-            const float z = acc[fm][fn][4 * g + e] + b + to_f32(__builtin_bit_cast(T, rb));
+            const float z = acc[fm][fn][4 * g + e] + b4[e] + to_f32(__builtin_bit_cast(T, rb));
             y[e] = to_f32(from_f32<T>(z));  // the value stored
             if (c < N && m < M) {
               s1 += (double)y[e];
@@ -867,75 +889,94 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       }
     });
   } else {
-    const bool has_bias = epi != EPI_DEFAULT;
+    // The bias slice of this tile (its BN columns, or its BM rows) goes to
+    // LDS once as fp32, zeros outside the matrix; each lane then reads the
+    // values of 4 consecutive columns with one 16-byte LDS read.  The element
+    // loop is compiled once per epilogue kind, so that it holds no run-time
+    // branches on the kind.
     const bool per_col = p.bias_per_col != 0;
-    const T* bias = (const T*)p.bias;
-    const bool gelu = epi == EPI_GELU_BIAS || epi == EPI_GELU_AUX_BIAS;
-    const bool relu = epi == EPI_RELU_BIAS || epi == EPI_RELU_AUX_BIAS;
-    static_for<FM>([&](auto fm_c) {
-      constexpr int fm = decltype(fm_c)::value;
-      const int rl = wrow0 + fm * 32 + lrow;
-      const int m = m0 + rl;
-      const float brow = (has_bias && !per_col && m < M) ? to_f32(bias[m]) : 0.0f;
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int cbase = n0 + wcol0 + fn * 32;
-        const int cgrp = cbase + 4 * khalf;
-        float y[16];
-        uint32_t bits = 0;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = cgrp + 8 * (r >> 2) + (r & 3);
-          float b = brow;
-          if (has_bias && per_col) b = c < N ? to_f32(bias[c]) : 0.0f;
-          const float z = acc[fm][fn][r] + b;
-          if (gelu) {
-            y[r] = gelu_erf(z);
-          } else if (relu) {
-            y[r] = z > 0.0f ? z : 0.0f;
-          } else {
-            y[r] = z;
-          }
-          if (epi == EPI_RELU_AUX_BIAS && z > 0.0f && c < N)
-            bits |= 1u << (8 * (r >> 2) + 4 * khalf + (r & 3));
-        }
-        stage(rl, wcol0 + fn * 32 + 4 * khalf, y);
-        if (epi == EPI_GELU_AUX_BIAS && m < M) {
-          // z = acc + bias, rounded, straight into aux: per (fm, fn) a row
-          // gets 32 contiguous columns from 4 stores of lanes l and l+32
-          T* zrow = (T*)p.aux + (size_t)m * p.ldo;
+    {
+      const T* bias = (const T*)p.bias;
+      const int len = per_col ? BN : BM, base = per_col ? n0 : m0, lim = per_col ? N : M;
+      for (int i = tid; i < len; i += NT)
+        bsl[i] = (epi != EPI_DEFAULT && base + i < lim) ? to_f32(bias[base + i]) : 0.0f;
+    }
+    __syncthreads();
+    auto run = [&](auto kind_c) {
+      constexpr int KIND = decltype(kind_c)::value;
+      constexpr bool gelu = KIND == EPI_GELU_BIAS || KIND == EPI_GELU_AUX_BIAS;
+      constexpr bool relu = KIND == EPI_RELU_BIAS || KIND == EPI_RELU_AUX_BIAS;
+      static_for<FM>([&](auto fm_c) {
+        constexpr int fm = decltype(fm_c)::value;
+        const int rl = wrow0 + fm * 32 + lrow;
+        const int m = m0 + rl;
+        const float brow = per_col ? 0.0f : bsl[rl];
+        static_for<FN>([&](auto fn_c) {
+          constexpr int fn = decltype(fn_c)::value;
+          const int cbase = n0 + wcol0 + fn * 32;
+          const int cl = wcol0 + fn * 32 + 4 * khalf;  // local column of element r = 0
+          float y[16], zs[16];
+          uint32_t bits = 0;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int c = cgrp + 8 * g;
-            float zz[4];
+            const f32x4 b4 = per_col ? *(const f32x4*)(bsl + cl + 8 * g) : f32x4{brow, brow, brow, brow};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float b = per_col ? (c + e < N ? to_f32(bias[c + e]) : 0.0f) : brow;
-              zz[e] = acc[fm][fn][4 * g + e] + b;
+              const int r = 4 * g + e;
+              const float z = acc[fm][fn][r] + b4[e];
+              zs[r] = z;
+              if constexpr (gelu)
+                y[r] = gelu_erf(z);
+              else if constexpr (relu)
+                y[r] = z > 0.0f ? z : 0.0f;
+              else
+                y[r] = z;
+              if constexpr (KIND == EPI_RELU_AUX_BIAS)
+                if (z > 0.0f && n0 + cl + 8 * g + e < N) bits |= 1u << (8 * g + 4 * khalf + e);
             }
-            if ((p.ldo & 3) == 0 && c + 3 < N) {
-              const u32x2 w = {pack2(zz[0], zz[1], T{}), pack2(zz[2], zz[3], T{})};
-              *(u32x2*)(zrow + c) = w;
-            } else {
+          }
+          stage(rl, cl, y);
+          if constexpr (KIND == EPI_GELU_AUX_BIAS) {
+            // z = acc + bias, rounded, straight into aux: per (fm, fn) a row
+            // gets 32 contiguous columns from 4 stores of lanes l and l+32
+            if (m < M) {
+              T* zrow = (T*)p.aux + (size_t)m * p.ldo;
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (c + e < N) zrow[c + e] = from_f32<T>(zz[e]);
+              for (int g = 0; g < 4; ++g) {
+                const int c = n0 + cl + 8 * g;
+                if ((p.ldo & 3) == 0 && c + 3 < N) {
+                  const u32x2 w = {pack2(zs[4 * g], zs[4 * g + 1], T{}),
+                                   pack2(zs[4 * g + 2], zs[4 * g + 3], T{})};
+                  *(u32x2*)(zrow + c) = w;
+                } else {
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    if (c + e < N) zrow[c + e] = from_f32<T>(zs[4 * g + e]);
+                }
+              }
             }
           }
-        }
-        if (epi == EPI_RELU_AUX_BIAS) {
-          // lanes l and l+32 hold complementary halves of row m's word
-          bits |= __shfl_xor(bits, 32);
-          if (khalf == 0 && m < M && cbase < N) {
-            uint32_t* mrow = p.aux + (size_t)m * p.aux_ld;
-            const int word = cbase >> 5;
-            mrow[word] = bits;
-            if (word == p.aux_words - 1)
-              for (int w = p.aux_words; w < p.aux_ld; ++w) mrow[w] = 0u;
+          if constexpr (KIND == EPI_RELU_AUX_BIAS) {
+            // lanes l and l+32 hold complementary halves of row m's word
+            bits |= __shfl_xor(bits, 32);
+            if (khalf == 0 && m < M && cbase < N) {
+              uint32_t* mrow = p.aux + (size_t)m * p.aux_ld;
+              const int word = cbase >> 5;
+              mrow[word] = bits;
+              if (word == p.aux_words - 1)
+                for (int w = p.aux_words; w < p.aux_ld; ++w) mrow[w] = 0u;
+            }
           }
-        }
-      }
-    });
+        });
+      });
+    };
+    switch (epi) {
+      case EPI_RELU_BIAS: run(std::integral_constant<int, EPI_RELU_BIAS>{}); break;
+      case EPI_RELU_AUX_BIAS: run(std::integral_constant<int, EPI_RELU_AUX_BIAS>{}); break;
+      case EPI_GELU_BIAS: run(std::integral_constant<int, EPI_GELU_BIAS>{}); break;
+      case EPI_GELU_AUX_BIAS: run(std::integral_constant<int, EPI_GELU_AUX_BIAS>{}); break;
+      default: run(std::integral_constant<int, EPI_BIAS>{}); break;  // DEFAULT: the bias slice is zero
+    }
   }
   __syncthreads();
 

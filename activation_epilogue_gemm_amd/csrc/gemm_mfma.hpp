@@ -25,13 +25,14 @@
 //   * LDS rows are XOR-swizzled in 16-byte units so that the 128-bit
 //     fragment reads (and the 64-bit transposing reads of a row-major [K,N]
 //     B) hit distinct banks of the 64-bank LDS;
-//   * v_mfma_f32_32x32x16_{f16,bf16}: exact products, fp32 accumulation.
-//     The B fragment is passed as the instruction's first operand and the A
-//     fragment as its second, so the accumulator holds the transposed tile:
-//     lane l, element r of a 32x32 tile is
+//   * v_mfma_f32_32x32x16_{f16,bf16} (kMfma below): exact products, fp32
+//     accumulation.  The B fragment is passed as the instruction's first
+//     operand and the A fragment as its second, so the accumulator holds the
+//     transposed block: lane l, element r of a 32x32 block is
 //         row m = l % 32,   column n = 8*(r/4) + 4*(l/32) + (r%4),
 //     i.e. each lane owns one output row and 4 runs of 4 consecutive
-//     columns, which become 8-byte stores.
+//     columns, which become 8-byte stores.  (With kMfma = 16, the 16x16x32
+//     form: row l % 16, columns 4*(l/16) + r.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -114,12 +115,35 @@ template <typename T> struct Frag;
 template <> struct Frag<_Float16> { using type = f16x8; };
 template <> struct Frag<__bf16> { using type = bf16x8; };
 
-__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma_op(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x16 mfma_op(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma_op(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_op(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The GEMM's MFMA shape: kMfma x kMfma output blocks, v_mfma_f32_32x32x16
+// (kMfma = 32) or v_mfma_f32_16x16x32 (kMfma = 16); every part of the kernel
+// is written for both.  The 16x16x32 form spends less energy per FLOP (in a
+// bare MFMA loop shaped like this kernel's it holds a ~14 % higher clock at
+// the power limit), but in the kernel the higher clock comes with a lower
+// busy share: measured against the vendor BLAS on one box, C3 is unchanged,
+// C4 gains 3 % and the FFN up-projections lose 3-11 %, so 32x32x16 stays.
+constexpr int kMfma = 32;
+constexpr int kAccN = kMfma * kMfma / 64;  // accumulator floats per lane per block
+constexpr int kLaneGroups = 64 / kMfma;    // lane groups l / kMfma
+constexpr int kKStep = 8 * kLaneGroups;    // k depth of one MFMA
+constexpr int kColStride = 4 * kLaneGroups;  // columns between a lane's 4-column groups
+template <int MT> struct AccOf;
+template <> struct AccOf<32> { using type = f32x16; };
+template <> struct AccOf<16> { using type = f32x4; };
+using AccBlock = typename AccOf<kMfma>::type;
 
 // 4 consecutive-k values of one column from a row-major [K,N] LDS tile:
 // within each group of 16 lanes, lane (4*h + q) points at row h, columns
@@ -237,7 +261,7 @@ struct GemmTile {
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int FM = WTM / 32, FN = WTN / 32;
+  static constexpr int FM = WTM / kMfma, FN = WTN / kMfma;
   static constexpr int KCH = BK / 8;                 // 16 B chunks per K-contiguous row
   static constexpr int NCH = BN / 8;                 // 16 B chunks per N-contiguous row
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
@@ -249,7 +273,7 @@ struct GemmTile {
   // rows sharing one 256-byte bank line
   static constexpr int RPK = (BK * 2 >= 256) ? 1 : 256 / (BK * 2);
   static constexpr int RPN = (BN * 2 >= 256) ? 1 : 256 / (BN * 2);
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 MFMA tiles");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32-row/32-column blocks");
   static_assert(BK % 16 == 0 && BK >= 32, "BK");
   static_assert(A_BYTES % (NT * 16) == 0 && B_BYTES % (NT * 16) == 0, "load split");
   static_assert(64 % KCH == 0 && 64 % NCH == 0 && BN * 2 <= 1024, "load split");
@@ -271,8 +295,16 @@ struct GemmTile {
   static __device__ __forceinline__ int swz_k(int r) { return (r / RPK) % KCH; }
   // 16 B-chunk swizzle of row r of the staged output tile
   static __device__ __forceinline__ int swz_o(int r) { return r % (BN / 8); }
-  // 16 B-chunk swizzle of an N-contiguous row kr (B stored [K,N])
-  static __device__ __forceinline__ int swz_n(int kr) { return (4 * (kr / RPN)) % NCH; }
+  // 16 B-chunk swizzle of an N-contiguous row kr (B stored [K,N]).  With
+  // 16x16x32 MFMAs, one transposing read of 32 lanes covers k rows h and
+  // h + 8 (h = 0..3) at the same columns; the swizzle gives those 8 rows 8
+  // distinct even chunk offsets within a 256-byte bank line (4 per line and
+  // two lines when 2 rows share one), so the 32 lanes hit 64 distinct banks.
+  // It repeats every 16 rows.
+  static __device__ __forceinline__ int swz_n(int kr) {
+    if constexpr (kMfma == 32) return (4 * (kr / RPN)) % NCH;
+    else return 2 * ((kr / RPN) % (4 / RPN)) + (8 / RPN) * ((kr / 8) % 2);
+  }
 };
 
 // A workgroup barrier that the instruction scheduler may not move any
@@ -378,29 +410,31 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     for (int j = 0; j < G::LPS; ++j) issue_one(kt, st, j);
   };
 
-  f32x16 acc[FM][FN];
+  AccBlock acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < kAccN; ++e) acc[i][j][e] = 0.0f;
 
-  const int lrow = lane & 31;   // row (A) / column (B) within a 32x32 MFMA tile
-  const int khalf = lane >> 5;  // which 8-wide k group of a 16-wide step
+  const int lrow = lane % kMfma;  // row (A) / column (B) within an MFMA block
+  const int lgrp = lane / kMfma;  // the lane's 8-wide k group of an MFMA step
 
   // A fragment (rows of A) and B fragment (columns of B) of k step ks of
   // the slab at sA.  The per-lane LDS offsets are computed once: fragment fm
   // (fn) and k step ks only add constants, because the swizzles repeat
   // every 32 K-contiguous rows and every 16 N-contiguous k rows.
-  constexpr int KS = BK / 16;
-  static_assert((32 / G::RPK) % KCH == 0, "A/B_T swizzle must repeat every 32 rows");
-  static_assert((4 * (16 / G::RPN)) % NCH == 0, "B swizzle must repeat every 16 k rows");
+  constexpr int KS = BK / kKStep;
+  static_assert(BK % kKStep == 0, "BK must be whole MFMA k steps");
+  static_assert((kMfma / G::RPK) % KCH == 0, "A/B_T swizzle must repeat every block of rows");
+  static_assert(kMfma == 16 ? (BT || G::RPN <= 2) : (4 * (16 / G::RPN)) % NCH == 0,
+                "B swizzle must repeat every 16 k rows");
   uint32_t a_lds[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int r = wm * WTM + lrow;
-    a_lds[ks] = (uint32_t)(r * BK * 2 + (((ks * 2 + khalf) ^ G::swz_k(r)) << 4));
+    a_lds[ks] = (uint32_t)(r * BK * 2 + (((ks * (kKStep / 8) + lgrp) ^ G::swz_k(r)) << 4));
   }
   constexpr int BL = BT ? KS : 2 * FN;
   uint32_t b_lds[BL];
@@ -408,30 +442,33 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int r = wn * WTN + lrow;
-      b_lds[ks] = (uint32_t)(G::A_BYTES + r * BK * 2 + (((ks * 2 + khalf) ^ G::swz_k(r)) << 4));
+      b_lds[ks] = (uint32_t)(G::A_BYTES + r * BK * 2 + (((ks * (kKStep / 8) + lgrp) ^ G::swz_k(r)) << 4));
     }
   } else {
     // two transposing reads per fragment: lane (g, i) = (lane / 16, lane % 16)
-    // reads k rows 8 (g / 2) + i / 4 (+ 4), columns 16 (g % 2) + 4 (i % 4) ..
+    // reads k rows 8 (g / CH) + i / 4 (+ 4), columns 16 (g % CH) + 4 (i % 4) ..,
+    // CH = kMfma / 16 column halves per block (a 16-lane group then holds
+    // column i of its 16 columns at 8 consecutive k)
+    constexpr int CH = kMfma / 16;
     const int g = lane >> 4, i = lane & 15;
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
-      const int ncol = wn * WTN + fn * 32 + (g & 1) * 16 + (i & 3) * 4;
+      const int ncol = wn * WTN + fn * kMfma + (g % CH) * 16 + (i & 3) * 4;
       const int nc = ncol >> 3, nb = (ncol & 7) * 2;
-      const int kr0 = (g >> 1) * 8 + (i >> 2), kr1 = kr0 + 4;
+      const int kr0 = (g / CH) * 8 + (i >> 2), kr1 = kr0 + 4;
       b_lds[2 * fn] = (uint32_t)(G::A_BYTES + kr0 * BN * 2 + ((nc ^ G::swz_n(kr0)) << 4) + nb);
       b_lds[2 * fn + 1] = (uint32_t)(G::A_BYTES + kr1 * BN * 2 + ((nc ^ G::swz_n(kr1)) << 4) + nb);
     }
   }
   auto read_a = [&](const uint8_t* sA, int ks, int fm) -> V8 {
-    return *(const V8*)(sA + a_lds[ks] + fm * 32 * BK * 2);
+    return *(const V8*)(sA + a_lds[ks] + fm * kMfma * BK * 2);
   };
   auto read_b = [&](const uint8_t* sA, int ks, int fn) -> V8 {
     if constexpr (BT) {
-      return *(const V8*)(sA + b_lds[ks] + fn * 32 * BK * 2);
+      return *(const V8*)(sA + b_lds[ks] + fn * kMfma * BK * 2);
     } else {
-      const u32x2 lo = lds_read_tr(sA + b_lds[2 * fn] + ks * 16 * BN * 2, T{});
-      const u32x2 hi = lds_read_tr(sA + b_lds[2 * fn + 1] + ks * 16 * BN * 2, T{});
+      const u32x2 lo = lds_read_tr(sA + b_lds[2 * fn] + ks * kKStep * BN * 2, T{});
+      const u32x2 hi = lds_read_tr(sA + b_lds[2 * fn + 1] + ks * kKStep * BN * 2, T{});
       const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
       return __builtin_bit_cast(V8, w);
     }
@@ -443,14 +480,14 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        acc[fm][fn] = mfma32(bf[fn], af[fm], acc[fm][fn]);
+        acc[fm][fn] = mfma_op(bf[fn], af[fm], acc[fm][fn]);
         between(fm * FN + fn);
       }
   };
 
   auto compute = [&](const uint8_t* sA) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       V8 af[FM], bf[FN];
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm) af[fm] = read_a(sA, ks, fm);
@@ -459,7 +496,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma32(bf[fn], af[fm], acc[fm][fn]);
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_op(bf[fn], af[fm], acc[fm][fn]);
     }
   };
 
@@ -479,7 +516,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     constexpr int A2_CH = A2_BYTES / (NT * 16);  // A loads per wave per pair
     constexpr int NA = 3;
     static_assert(A2_BYTES % (NT * 16) == 0 && 64 % KCH2 == 0, "load split");
-    static_assert((32 / RPK2) % KCH2 == 0, "A swizzle must repeat every 32 rows");
+    static_assert((kMfma / RPK2) % KCH2 == 0, "A swizzle must repeat every block of rows");
     static_assert(A2_CH + G::B_CH <= FM * FN * KS, "one load after each MFMA");
     auto swz2 = [](int r) { return (r / RPK2) % KCH2; };
     uint8_t* const a_ring = smem;
@@ -516,7 +553,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int r = wm * WTM + lrow;
-        const int chunk = h * (BK / 8) + ks * 2 + khalf;
+        const int chunk = h * (BK / 8) + ks * (kKStep / 8) + lgrp;
         a2_lds[h][ks] = (uint32_t)(r * BK2 * 2 + ((chunk ^ swz2(r)) << 4));
       }
     // prologue, in this order (the waits count on it): A pair 0, B slabs 0
@@ -548,7 +585,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
           for (int fm = 0; fm < FM; ++fm)
-            af[ks][fm] = *(const V8*)(sa + a2_lds[h][ks] + fm * 32 * BK2 * 2);
+            af[ks][fm] = *(const V8*)(sa + a2_lds[h][ks] + fm * kMfma * BK2 * 2);
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) bf[ks][fn] = read_b(sb, ks, fn);
         }
@@ -587,7 +624,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // Ping-pong.  Waves w and w + 4 of the workgroup share a SIMD; they are
     // in the two groups grp = w / 4.  Each wave alternates a load phase -- read
     // all of its fragments of slab kt into registers, wait for its share of
-    // slab kt + 1 -- and a compute phase of FM * FN * BK / 16 MFMAs on
+    // slab kt + 1 -- and a compute phase of FM * FN * KS MFMAs on
     // registers, between which it issues its share of the slab NS - 1
     // ahead.  Group 1 starts one phase late, so while one group multiplies
     // the other loads, and the barrier that ends a phase only hands the
@@ -659,7 +696,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   // Nothing waits on another workgroup, so no ordering of the workgroups
   // can stall the grid.
   if (p.splits > 1) {
-    constexpr int QE = FM * FN * 16;  // floats per thread
+    constexpr int QE = FM * FN * kAccN;  // floats per thread
     float* const slots = p.ws + (size_t)tile_id * p.splits * (BM * BN);
     float* const own = slots + (size_t)split * (QE * NT);
     static_for<FM>([&](auto fm_c) {
@@ -667,8 +704,8 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __hip_atomic_store(own + ((fm * FN + fn) * 16 + r) * NT + tid, acc[fm][fn][r],
+        for (int r = 0; r < kAccN; ++r)
+          __hip_atomic_store(own + ((fm * FN + fn) * kAccN + r) * NT + tid, acc[fm][fn][r],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     });
     wait_vmcnt<0>();  // this thread's slot stores are complete
@@ -689,24 +726,25 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     if (is_last == 0u) return;  // uniform over the workgroup
     // one slot per pass, in steps of 16 or 32 independent loads (hoisting
     // all loads of a slot would spill the accumulators)
-    constexpr int FNG = FN > 2 ? 1 : FN;  // accumulator blocks per step
+    constexpr int FNG = kAccN == 16 ? (FN > 2 ? 1 : FN) : (FN > 4 ? 4 : FN);  // blocks per step
+    static_assert(FN % FNG == 0, "split-K load steps");
     for (int s = 0; s < p.splits; ++s) {
       const float* src = slots + (size_t)s * (QE * NT);
       static_for<FM>([&](auto fm_c) {
         constexpr int fm = decltype(fm_c)::value;
 #pragma unroll
         for (int f0 = 0; f0 < FN; f0 += FNG) {
-          float v[FNG][16];
+          float v[FNG][kAccN];
 #pragma unroll
           for (int j = 0; j < FNG; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              v[j][r] = __hip_atomic_load(src + ((fm * FN + f0 + j) * 16 + r) * NT + tid,
+            for (int r = 0; r < kAccN; ++r)
+              v[j][r] = __hip_atomic_load(src + ((fm * FN + f0 + j) * kAccN + r) * NT + tid,
                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
           for (int j = 0; j < FNG; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < kAccN; ++r)
               acc[fm][f0 + j][r] = (s == 0 ? 0.0f : acc[fm][f0 + j][r]) + v[j][r];
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -715,12 +753,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   }
 
   // ---- epilogue on the accumulators -----------------------------------------
-  // lane owns local row rl = wrow0 + 32 fm + lrow and, in tile (fm, fn), the
-  // columns cl + 8 g + {0,1,2,3} (g = 0..3, elements r = 4 g + e) with
-  // cl = wcol0 + 32 fn + 4 khalf.  The results are rounded into an LDS copy
-  // of the output tile (free since the main loop's last barrier) and then
-  // written to HBM row by row with 16-byte stores: written straight from the
-  // accumulator layout, every store instruction would touch 64 rows.
+  // In block (fm, fn) a lane owns local row rl = wrow0 + kMfma fm + lrow and
+  // the columns cl + kColStride g + {0,1,2,3} (g < kAccN / 4, element
+  // r = 4 g + e), with cl = wcol0 + kMfma fn + 4 lgrp.  The results are
+  // rounded into an LDS copy of the output tile (free since the main loop's
+  // last barrier) and then written to HBM row by row with 16-byte stores:
+  // written straight from the accumulator layout, every store instruction
+  // would touch 16 or 32 rows.
   const int epi = p.epi;
   const int wrow0 = wm * WTM;
   const int wcol0 = wn * WTN;
@@ -728,11 +767,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   float* const red = (float*)(smem + G::OUT_BYTES);          // [WM][BN] fp32
   float* const bsl = (float*)(smem + G::OUT_BYTES + G::RED_BYTES);  // bias slice, fp32
 
-  auto stage = [&](int rl, int cl, const float (&y)[16]) {
+  constexpr int NG = kAccN / 4;         // 4-column groups per lane and block
+  constexpr int BPW = 32 / kMfma;       // blocks per 32-column mask word
+  auto stage = [&](int rl, int cl, const float (&y)[kAccN]) {
     uint8_t* row = so + rl * (BN * 2) + (cl & 7) * 2;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int c = cl + 8 * g;
+    for (int g = 0; g < NG; ++g) {
+      const int c = cl + kColStride * g;
       const u32x2 w = {pack2(y[4 * g], y[4 * g + 1], T{}), pack2(y[4 * g + 2], y[4 * g + 3], T{})};
       *(u32x2*)(row + (((c >> 3) ^ G::swz_o(rl)) << 4)) = w;
     }
@@ -776,23 +817,23 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       load_tile((const T*)p.aux);
       __syncthreads();
     }
-    float cs[FN][16];
+    float cs[FN][kAccN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) cs[fn][r] = 0.0f;
+      for (int r = 0; r < kAccN; ++r) cs[fn][r] = 0.0f;
     static_for<FM>([&](auto fm_c) {
       constexpr int fm = decltype(fm_c)::value;
-      const int rl = wrow0 + fm * 32 + lrow;
+      const int rl = wrow0 + fm * kMfma + lrow;
       const int m = m0 + rl;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int cbase = n0 + wcol0 + fn * 32;
-        float y[16];
+        const int cl = wcol0 + fn * kMfma + 4 * lgrp;  // local column of element r = 0
+        float y[kAccN];
         if (dgelu) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const u32x2 zw = *(const u32x2*)staged4(rl, wcol0 + fn * 32 + 4 * khalf + 8 * g);
+          for (int g = 0; g < NG; ++g) {
+            const u32x2 zw = *(const u32x2*)staged4(rl, cl + kColStride * g);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint16_t zb = (uint16_t)(zw[e >> 1] >> (16 * (e & 1)));
@@ -801,39 +842,38 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
             }
           }
         } else {
-          const uint32_t mw = (m < M && cbase < N)
-                                  ? p.aux[(size_t)m * p.aux_ld + (cbase >> 5)] >> (4 * khalf)
-                                  : 0u;
+          // the mask word holding this block's columns, shifted to the
+          // lane's first column (a block never straddles a word)
+          const int c0 = n0 + cl;
+          const uint32_t mw = (m < M && c0 < N) ? p.aux[(size_t)m * p.aux_ld + (c0 >> 5)] >> (c0 & 31)
+                                                : 0u;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int bit = 8 * (r >> 2) + (r & 3);
+          for (int r = 0; r < kAccN; ++r) {
+            const int bit = kColStride * (r >> 2) + (r & 3);
             y[r] = ((mw >> bit) & 1u) ? acc[fm][fn][r] : 0.0f;
           }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cs[fn][r] += y[r];
-        stage(rl, wcol0 + fn * 32 + 4 * khalf, y);
+        for (int r = 0; r < kAccN; ++r) cs[fn][r] += y[r];
+        stage(rl, cl, y);
       }
     });
-    // sum over the 32 rows held by the lanes with the same khalf
+    // sum over the rows held by the lanes of the same lane group
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < kAccN; ++r) {
         float v = cs[fn][r];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        v += __shfl_xor(v, 16);
+#pragma unroll
+        for (int o = 1; o < kMfma; o <<= 1) v += __shfl_xor(v, o);
         cs[fn][r] = v;
       }
     if (lrow == 0) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          red[wm * BN + wn * WTN + fn * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3)] = cs[fn][r];
+        for (int r = 0; r < kAccN; ++r)
+          red[wm * BN + wcol0 + fn * kMfma + kColStride * (r >> 2) + 4 * lgrp + (r & 3)] = cs[fn][r];
     }
   } else if (epi == EPI_BIAS_RES_SUMS) {
     // y = acc + bias[n] + residual[m, n].  The residual tile is first copied
@@ -852,15 +892,15 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     double* red64 = (double*)(smem + G::OUT_BYTES);  // [WN][BM][2]
     static_for<FM>([&](auto fm_c) {
       constexpr int fm = decltype(fm_c)::value;
-      const int rl = wrow0 + fm * 32 + lrow;
+      const int rl = wrow0 + fm * kMfma + lrow;
       const int m = m0 + rl;
       double s1 = 0.0, s2 = 0.0;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int cl = wcol0 + fn * 32 + 4 * khalf;
+        const int cl = wcol0 + fn * kMfma + 4 * lgrp;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c_loc = cl + 8 * g;
+        for (int g = 0; g < NG; ++g) {
+          const int c_loc = cl + kColStride * g;
           uint8_t* at = staged4(rl, c_loc);
           const u32x2 rw = *(const u32x2*)at;
           const f32x4 b4 = *(const f32x4*)(bsl + c_loc);
@@ -880,10 +920,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           *(u32x2*)at = w;
         }
       }
-      // lanes l and l + 32 hold the two column halves of row rl
-      s1 += __shfl_xor(s1, 32);
-      s2 += __shfl_xor(s2, 32);
-      if (khalf == 0) {
+      // the lanes with the same lrow hold the row's other column groups
+#pragma unroll
+      for (int o = kMfma; o < 64; o <<= 1) {
+        s1 += __shfl_xor(s1, o);
+        s2 += __shfl_xor(s2, o);
+      }
+      if (lgrp == 0) {
         red64[(wn * BM + rl) * 2] = s1;
         red64[(wn * BM + rl) * 2 + 1] = s2;
       }
@@ -908,18 +951,18 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       constexpr bool relu = KIND == EPI_RELU_BIAS || KIND == EPI_RELU_AUX_BIAS;
       static_for<FM>([&](auto fm_c) {
         constexpr int fm = decltype(fm_c)::value;
-        const int rl = wrow0 + fm * 32 + lrow;
+        const int rl = wrow0 + fm * kMfma + lrow;
         const int m = m0 + rl;
         const float brow = per_col ? 0.0f : bsl[rl];
+        uint32_t wbits = 0;  // mask word being assembled (BPW blocks)
         static_for<FN>([&](auto fn_c) {
           constexpr int fn = decltype(fn_c)::value;
-          const int cbase = n0 + wcol0 + fn * 32;
-          const int cl = wcol0 + fn * 32 + 4 * khalf;  // local column of element r = 0
-          float y[16], zs[16];
-          uint32_t bits = 0;
+          const int cl = wcol0 + fn * kMfma + 4 * lgrp;  // local column of element r = 0
+          float y[kAccN], zs[kAccN];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 b4 = per_col ? *(const f32x4*)(bsl + cl + 8 * g) : f32x4{brow, brow, brow, brow};
+          for (int g = 0; g < NG; ++g) {
+            const f32x4 b4 = per_col ? *(const f32x4*)(bsl + cl + kColStride * g)
+                                     : f32x4{brow, brow, brow, brow};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 4 * g + e;
@@ -931,19 +974,21 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
                 y[r] = z > 0.0f ? z : 0.0f;
               else
                 y[r] = z;
-              if constexpr (KIND == EPI_RELU_AUX_BIAS)
-                if (z > 0.0f && n0 + cl + 8 * g + e < N) bits |= 1u << (8 * g + 4 * khalf + e);
+              if constexpr (KIND == EPI_RELU_AUX_BIAS) {
+                const int c = n0 + cl + kColStride * g + e;
+                if (z > 0.0f && c < N) wbits |= 1u << (c & 31);
+              }
             }
           }
           stage(rl, cl, y);
           if constexpr (KIND == EPI_GELU_AUX_BIAS) {
-            // z = acc + bias, rounded, straight into aux: per (fm, fn) a row
-            // gets 32 contiguous columns from 4 stores of lanes l and l+32
+            // z = acc + bias, rounded, straight into aux: 8-byte stores of
+            // 4 consecutive columns per lane and group
             if (m < M) {
               T* zrow = (T*)p.aux + (size_t)m * p.ldo;
 #pragma unroll
-              for (int g = 0; g < 4; ++g) {
-                const int c = n0 + cl + 8 * g;
+              for (int g = 0; g < NG; ++g) {
+                const int c = n0 + cl + kColStride * g;
                 if ((p.ldo & 3) == 0 && c + 3 < N) {
                   const u32x2 w = {pack2(zs[4 * g], zs[4 * g + 1], T{}),
                                    pack2(zs[4 * g + 2], zs[4 * g + 3], T{})};
@@ -956,16 +1001,19 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
               }
             }
           }
-          if constexpr (KIND == EPI_RELU_AUX_BIAS) {
-            // lanes l and l+32 hold complementary halves of row m's word
-            bits |= __shfl_xor(bits, 32);
-            if (khalf == 0 && m < M && cbase < N) {
+          if constexpr (KIND == EPI_RELU_AUX_BIAS && (fn + 1) % BPW == 0) {
+            // the word's other bits are held by the lanes with the same lrow
+#pragma unroll
+            for (int o = kMfma; o < 64; o <<= 1) wbits |= __shfl_xor(wbits, o);
+            const int cword = n0 + wcol0 + (fn + 1 - BPW) * kMfma;  // first column of the word
+            if (lgrp == 0 && m < M && cword < N) {
               uint32_t* mrow = p.aux + (size_t)m * p.aux_ld;
-              const int word = cbase >> 5;
-              mrow[word] = bits;
+              const int word = cword >> 5;
+              mrow[word] = wbits;
               if (word == p.aux_words - 1)
                 for (int w = p.aux_words; w < p.aux_ld; ++w) mrow[w] = 0u;
             }
+            wbits = 0;
           }
         });
       });
@@ -1036,7 +1084,7 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
   static_assert(SCHED >= 0 && SCHED <= 2, "schedule");
   static_assert(SCHED == 0 || WM * WN == 8, "ping-pong pairs waves w and w + 4 on each SIMD");
   static_assert(SCHED != 1 || NS >= 3, "ping-pong issues each slab NS - 1 ahead from a compute phase");
-  static_assert(SCHED != 1 || (BK / 16) * (BM / WM / 32) * (BN / WN / 32) >=
+  static_assert(SCHED != 1 || (BK / kKStep) * (BM / WM / kMfma) * (BN / WN / kMfma) >=
                                   GemmTile<BM, BN, BK, WM, WN, NS>::LPS,
                 "ping-pong issues one load after each MFMA of a compute phase");
   const int blocks = a.tiles_m * a.tiles_n * (a.splits > 1 ? a.splits : 1);

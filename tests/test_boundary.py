@@ -319,3 +319,69 @@ def test_split_execute_validation():
         assert "splits=2" in p.info()
         assert lib.gemmepi_autotune(p._h, 4096, 4096, 4096, None, 4096, 3, None, None) == \
             ge.ERR_UNSUPPORTED
+
+
+def test_plan_cache_is_thread_safe():
+    """Eight threads plan and destroy overlapping keys at once (ctypes drops
+    the GIL during each call); every call succeeds and the cache is left
+    usable, with each key's entry freed or shared consistently."""
+    import random
+    import threading
+    lib = ge.library()
+    shapes = [(64, 64, 64), (128, 256, 512), (1000, 1000, 1000), (1, 4096, 4096), (2048, 11008, 4096)]
+    failures = []
+
+    def worker(seed):
+        rng = random.Random(seed)
+        held = []
+        for _ in range(400):
+            M, N, K = rng.choice(shapes)
+            h = ctypes.c_void_p()
+            st = lib.gemmepi_plan(ctypes.byref(h), M, N, K, 0, 1, rng.choice([0, 1]))
+            if st != ge.OK:
+                failures.append(("plan", st))
+                continue
+            held.append(h)
+            if len(held) > 4:
+                st = lib.gemmepi_plan_destroy(held.pop(rng.randrange(len(held))))
+                if st != ge.OK:
+                    failures.append(("destroy", st))
+        for h in held:
+            if lib.gemmepi_plan_destroy(h) != ge.OK:
+                failures.append(("destroy", -1))
+
+    threads = [threading.Thread(target=worker, args=(s,)) for s in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert failures == []
+    for M, N, K in shapes:
+        p = ge.plan(M, N, K, "f16", "BIAS", 0)
+        assert "M=%d" % M in p.info()
+        p.destroy()
+
+
+def test_last_error_is_per_thread():
+    """A failing call's detail stays with its own thread."""
+    import threading
+    lib = ge.library()
+    seen = {}
+
+    def bad():
+        h = ctypes.c_void_p()
+        seen["bad_status"] = lib.gemmepi_plan(ctypes.byref(h), 64, 64, 7, 0, 1, 0)
+        seen["bad"] = ge.last_error()
+
+    def good():
+        h = ctypes.c_void_p()
+        seen["good_status"] = lib.gemmepi_plan(ctypes.byref(h), 64, 64, 64, 0, 1, 0)
+        seen["good"] = ge.last_error()
+        lib.gemmepi_plan_destroy(h)
+
+    for fn in (bad, good):
+        t = threading.Thread(target=fn)
+        t.start()
+        t.join()
+    assert seen["bad_status"] == ge.ERR_MISALIGNED and "K=7" in seen["bad"]
+    assert seen["good_status"] == ge.OK and "K=7" not in seen["good"]

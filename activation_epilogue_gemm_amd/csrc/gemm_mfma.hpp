@@ -180,45 +180,39 @@ __device__ __forceinline__ uint32_t pack2(float a, float b, __bf16) {
 // erf is evaluated with Abramowitz & Stegun, Handbook of Mathematical
 // Functions, formula 7.1.26 (|error| <= 1.5e-7 for x >= 0):
 //   erf(x) = 1 - q,  q = (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
-//   t = 1 / (1 + p x).
-// With x = |z| / sqrt 2 this gives 1 + erf(z/sqrt 2) = 2 - q for z >= 0 and
-// q for z < 0, so the negative branch keeps full relative accuracy.
-// Branch-free, about a dozen VALU operations.
-__device__ __forceinline__ float one_plus_erf_scaled(float z) {  // 1 + erf(z / sqrt 2)
-  const float x = fabsf(z) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  // exp(-x^2) = 2^(-x^2 log2 e)
-  const float q = poly * __builtin_amdgcn_exp2f(-x * x * 1.44269504088896340736f);
-  return z >= 0.0f ? 2.0f - q : q;
-}
-// gelu(z) itself, from the same formula with fewer operations.  With
-// h = Phi(-|z|) = erfc(|z| / sqrt 2) / 2:
-//   z >= 0: z Phi(z) = z - z h,   z < 0: z Phi(z) = z h = -|z| h,
-// so gelu(z) = max(z, 0) - |z| h.  h is 7.1.26's q / 2 (coefficients
-// halved), and with u = |z| sqrt(log2(e) / 2) the exponential is 2^(-u^2)
-// and p x = (p / sqrt(log2 e)) u: 11 VALU operations and two
-// transcendentals per element.
-__device__ __forceinline__ float gelu_erf(float z) {
+//   t = 1 / (1 + p x),
+// taken at x = |z| / sqrt 2.  Both functions below use
+//   h = Phi(-|z|) = erfc(|z| / sqrt 2) / 2 = q / 2,
+// computed directly (not as 1 - something), so the negative branch keeps
+// full relative accuracy.  The halving is folded into the coefficients,
+// and with u = |z| sqrt(log2(e) / 2) the exponential exp(-z^2 / 2) is
+// 2^(-u^2) and p x = (p / sqrt(log2 e)) u.
+struct ErfcHalf {
+  float h;  // Phi(-|z|)
+  float e;  // exp(-z^2 / 2)
+};
+__device__ __forceinline__ ErfcHalf erfc_half(float z) {
   const float u = fabsf(z) * 0.8493218002880191f;
   const float t = __builtin_amdgcn_rcpf(fmaf(0.2727374808792225f, u, 1.0f));
   float poly = fmaf(0.5307027145f, t, -0.7265760135f);
   poly = fmaf(poly, t, 0.7107068705f);
   poly = fmaf(poly, t, -0.142248368f);
   poly = fmaf(poly, t, 0.127414796f);
-  const float h = poly * t * __builtin_amdgcn_exp2f(-(u * u));
-  return fmaf(-fabsf(z), h, fmaxf(z, 0.0f));
+  const float e = __builtin_amdgcn_exp2f(-(u * u));
+  return {poly * t * e, e};
 }
-
-// gelu'(z) = Phi(z) + z phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi), with Phi
-// from the same erf evaluation.
+// z >= 0: z Phi(z) = z - z h,   z < 0: z Phi(z) = z h = -|z| h,
+// so gelu(z) = max(z, 0) - |z| h: 11 VALU operations and two
+// transcendentals per element.
+__device__ __forceinline__ float gelu_erf(float z) {
+  return fmaf(-fabsf(z), erfc_half(z).h, fmaxf(z, 0.0f));
+}
+// gelu'(z) = Phi(z) + z phi(z), phi(z) = exp(-z^2 / 2) / sqrt(2 pi): the
+// exponential of phi is the one the erf evaluation already computed.
 __device__ __forceinline__ float gelu_grad(float z) {
-  const float phi = 0.39894228040143267794f * __builtin_amdgcn_exp2f(-0.72134752044448170368f * z * z);
-  return fmaf(z, phi, 0.5f * one_plus_erf_scaled(z));
+  const ErfcHalf r = erfc_half(z);
+  const float Phi = z >= 0.0f ? 1.0f - r.h : r.h;
+  return fmaf(z * 0.3989422804014327f, r.e, Phi);
 }
 
 // blockIdx -> output tile.  The hardware hands consecutive workgroup ids

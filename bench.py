@@ -256,7 +256,7 @@ def cpu_baseline(seconds_target=12.0):
     B = c.host_B()
     rows_all = wl.sample_rows(c.M, 32768, wl.row_sample_seed(3))
     # calibrate: a small warm-up call (thread pools, page faults), then a
-    # 512-row probe; size the timed sample to ~seconds_target from the probe
+    # 4096-row probe; size the timed sample to ~seconds_target from the probe
     def run(rs):
         A_rs = c.host_A(rs)
         t = time.perf_counter()

@@ -500,9 +500,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // 64 bytes, half a 128-byte line per row; a 64-wide A slab gives 8 rows
     // x 128 bytes.  A lives in a ring of 3 double slabs (pair q = slabs 2q,
     // 2q + 1 of the range), B in a ring of 4 slabs, 160 KiB together.  The
-    // compute phase of slab i issues B slab i + 3 and, after an odd slab, A
-    // pair (i + 3) / 2, so a load phase may leave in flight exactly the
-    // loads of the previous compute phase: B's, plus A's after an odd slab.
+    // load phase of slab i issues B slab i + 3 and, in the second slab of a
+    // pair, A pair q + 2 (see the loop).  The compute phases issue nothing
+    // but MFMAs.
     static_assert(SCHED != 2 || NS == 4, "schedule 2 issues B three slabs ahead");
     constexpr int BK2 = 2 * BK, KCH2 = BK2 / 8, RPB2 = 1024 / (BK2 * 2);
     constexpr int RPK2 = (BK2 * 2 >= 256) ? 1 : 256 / (BK2 * 2);
@@ -511,7 +511,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     constexpr int NA = 3;
     static_assert(A2_BYTES % (NT * 16) == 0 && 64 % KCH2 == 0, "load split");
     static_assert((kMfma / RPK2) % KCH2 == 0, "A swizzle must repeat every block of rows");
-    static_assert(A2_CH + G::B_CH <= FM * FN * KS, "one load after each MFMA");
+    static_assert(A2_CH + 2 * G::B_CH < 64, "vmcnt range");
     auto swz2 = [](int r) { return (r / RPK2) % KCH2; };
     uint8_t* const a_ring = smem;
     uint8_t* const b_ring = smem + NA * A2_BYTES;
@@ -583,22 +583,27 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) bf[ks][fn] = read_b(sb, ks, fn);
         }
-        wait_vmcnt<(h == 0) ? A2_CH + G::B_CH : G::B_CH>();
-        phase_barrier();
+        // The load phase also issues this wave's loads of B slab i + 3 and,
+        // in the second slab of a pair, of A pair q + 2, after its fragment
+        // reads.  Each load written straight to LDS holds up the issuing
+        // wave for ~25 cycles; here that wave would otherwise idle at the
+        // barrier, while in the compute phase it delayed the MFMAs.  The
+        // stages are free: slab i - 1 and pair q - 1 were last read in the
+        // other group's load phase before the last barrier.  A load issued
+        // in load phase s is waited for two load phases later, so at this
+        // wait the loads of this phase and the previous one may stay in
+        // flight (between them one A pair and two B slabs).
         const int a_next = (a_cur + 2 >= NA) ? a_cur + 2 - NA : a_cur + 2;
+        if constexpr (h == 1) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          mfma_step(af[ks], bf[ks], [&](int qq) {
-            const int d = ks * FM * FN + qq;
-            if constexpr (h == 1) {
-              if (d < A2_CH)
-                issue_a2(q + 2, a_next, d);
-              else if (d < A2_CH + G::B_CH)
-                issue_b2(kt_begin + i + 3, (i + 3) & 3, d - A2_CH);
-            } else {
-              if (d < G::B_CH) issue_b2(kt_begin + i + 3, (i + 3) & 3, d);
-            }
-          });
+          for (int j = 0; j < A2_CH; ++j) issue_a2(q + 2, a_next, j);
+        }
+#pragma unroll
+        for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + i + 3, (i + 3) & 3, j);
+        wait_vmcnt<A2_CH + 2 * G::B_CH>();
+        phase_barrier();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) mfma_step(af[ks], bf[ks], [&](int) {});
         phase_barrier();
       });
       a_cur = (a_cur + 1 == NA) ? 0 : a_cur + 1;

@@ -501,8 +501,9 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // x 128 bytes.  A lives in a ring of 3 double slabs (pair q = slabs 2q,
     // 2q + 1 of the range), B in a ring of 4 slabs, 160 KiB together.  The
     // load phase of slab i issues B slab i + 3 and, in the second slab of a
-    // pair, A pair q + 2 (see the loop).  The compute phases issue nothing
-    // but MFMAs.
+    // pair, A pair q + 2 (see the loop).  B stored [N,K] is fetched in pairs
+    // too, in a ring of 2 (below).  The compute phases issue nothing but
+    // MFMAs.
     static_assert(SCHED != 2 || NS == 4, "schedule 2 issues B three slabs ahead");
     constexpr int BK2 = 2 * BK, KCH2 = BK2 / 8, RPB2 = 1024 / (BK2 * 2);
     constexpr int RPK2 = (BK2 * 2 >= 256) ? 1 : 256 / (BK2 * 2);
@@ -515,6 +516,40 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     auto swz2 = [](int r) { return (r / RPK2) % KCH2; };
     uint8_t* const a_ring = smem;
     uint8_t* const b_ring = smem + NA * A2_BYTES;
+    // B stored [N,K] is K-contiguous as well and is then also fetched in
+    // double-wide slabs, in a ring of 2 pairs: pair q + 1 goes into the
+    // stage of pair q - 1 in the first load phase after that stage is free
+    // (that of slab 2q) and is waited for in the next one (slab 2q + 1).
+    // Its loads have half the time to land that A's have, but every B load
+    // instruction then reads 8 whole 128-byte lines instead of 16 halves
+    // (measured on the [N,K] form of the 65536 x 8192 x 16384 GEMM: +10 %).
+    constexpr bool BPAIR = BT;
+    constexpr int B2_BYTES = BN * BK2 * 2;
+    constexpr int B2_CH = B2_BYTES / (NT * 16);  // B loads per wave per pair
+    static_assert(!BPAIR || (B2_BYTES % (NT * 16) == 0 && NA * A2_BYTES + 2 * B2_BYTES <= SMEM_BYTES),
+                  "B pair ring");
+    static_assert(!BPAIR || A2_CH + B2_CH < 64, "vmcnt range");
+    uint32_t b2_off[BPAIR ? B2_CH : 1];
+    int b2_k[BPAIR ? B2_CH : 1];
+    uint32_t b2_lds[2][KS];
+    if constexpr (BPAIR) {
+#pragma unroll
+      for (int i = 0; i < B2_CH; ++i) {
+        const int blk = i * NW + wave;
+        const int r = blk * RPB2 + lane / KCH2;
+        const int kc = (lane % KCH2) ^ swz2(r);
+        b2_off[i] = (n0 + r < N) ? (uint32_t)((r * p.ldb + kc * 8) * 2) : kOOB;
+        b2_k[i] = kc * 8;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int r = wn * WTN + lrow;
+          const int chunk = h * (BK / 8) + ks * (kKStep / 8) + lgrp;
+          b2_lds[h][ks] = (uint32_t)(r * BK2 * 2 + ((chunk ^ swz2(r)) << 4));
+        }
+    }
     uint32_t a2_off[A2_CH];
     int a2_k[A2_CH];
 #pragma unroll
@@ -536,6 +571,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (size_t)k0 * 2);
       buffer_load16_lds(rA, st_addr + (j * NW + wave) * 1024, a2_off[j] | kill);
     };
+    auto issue_bp = [&](int q, int stage, int j) {
+      const int slab0 = kt_begin + 2 * q;
+      const bool none = slab0 >= kt_end;
+      const int k0 = none ? 0 : slab0 * BK;
+      const uint32_t st_addr =
+          __builtin_amdgcn_readfirstlane(lds_addr_of(b_ring + stage * B2_BYTES));
+      const uint32_t kill = (none || k0 + b2_k[j] >= k_stop) ? kOOB : 0u;
+      const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + (size_t)k0 * 2);
+      buffer_load16_lds(rB, st_addr + (j * NW + wave) * 1024, b2_off[j] | kill);
+    };
     // B slab kt into B stage `stage` through the schedule-1 loader (its B
     // offsets are relative to a stage whose A part is A_BYTES long)
     auto issue_b2 = [&](int kt, int stage, int j) {
@@ -550,6 +595,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         const int chunk = h * (BK / 8) + ks * (kKStep / 8) + lgrp;
         a2_lds[h][ks] = (uint32_t)(r * BK2 * 2 + ((chunk ^ swz2(r)) << 4));
       }
+    if constexpr (BPAIR) {
+      // prologue: A pair 0, B pair 0, A pair 1; then wait for pair 0
+#pragma unroll
+      for (int j = 0; j < A2_CH; ++j) issue_a2(0, 0, j);
+#pragma unroll
+      for (int j = 0; j < B2_CH; ++j) issue_bp(0, 0, j);
+#pragma unroll
+      for (int j = 0; j < A2_CH; ++j) issue_a2(1, 1, j);
+      wait_vmcnt<A2_CH>();
+    } else {
     // prologue, in this order (the waits count on it): A pair 0, B slabs 0
     // and 1, A pair 1, B slab 2; then wait for slab 0
 #pragma unroll
@@ -563,6 +618,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
     for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + 2, 2, j);
     wait_vmcnt<G::B_CH + A2_CH + G::B_CH>();
+    }
     __syncthreads();
     const int grp = wave >> 2;
     if (grp == 1) phase_barrier();
@@ -574,6 +630,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         const int i = 2 * q + h;  // slab index in the range
         const uint8_t* sa = a_ring + a_cur * A2_BYTES;
         const uint8_t* sb = b_ring + (i & 3) * G::B_BYTES - G::A_BYTES;
+        const uint8_t* sbp = b_ring + (q & 1) * B2_BYTES;
         V8 af[KS][FM], bf[KS][FN];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -581,7 +638,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           for (int fm = 0; fm < FM; ++fm)
             af[ks][fm] = *(const V8*)(sa + a2_lds[h][ks] + fm * kMfma * BK2 * 2);
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) bf[ks][fn] = read_b(sb, ks, fn);
+          for (int fn = 0; fn < FN; ++fn) {
+            if constexpr (BPAIR)
+              bf[ks][fn] = *(const V8*)(sbp + b2_lds[h][ks] + fn * kMfma * BK2 * 2);
+            else
+              bf[ks][fn] = read_b(sb, ks, fn);
+          }
         }
         // The load phase also issues this wave's loads of B slab i + 3 and,
         // in the second slab of a pair, of A pair q + 2, after its fragment
@@ -594,6 +656,21 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         // wait the loads of this phase and the previous one may stay in
         // flight (between them one A pair and two B slabs).
         const int a_next = (a_cur + 2 >= NA) ? a_cur + 2 - NA : a_cur + 2;
+        if constexpr (BPAIR) {
+          // first slab of pair q: B pair q + 1 into the stage of pair q - 1;
+          // second slab: A pair q + 2.  The wait of the second slab leaves
+          // only that A pair in flight, so B pair q + 1 and A pair q + 1
+          // have landed before slab 2q + 2 is read.
+          if constexpr (h == 0) {
+#pragma unroll
+            for (int j = 0; j < B2_CH; ++j) issue_bp(q + 1, (q + 1) & 1, j);
+            wait_vmcnt<A2_CH + B2_CH>();
+          } else {
+#pragma unroll
+            for (int j = 0; j < A2_CH; ++j) issue_a2(q + 2, a_next, j);
+            wait_vmcnt<A2_CH>();
+          }
+        } else {
         if constexpr (h == 1) {
 #pragma unroll
           for (int j = 0; j < A2_CH; ++j) issue_a2(q + 2, a_next, j);
@@ -601,6 +678,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
         for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + i + 3, (i + 3) & 3, j);
         wait_vmcnt<A2_CH + 2 * G::B_CH>();
+        }
         phase_barrier();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) mfma_step(af[ks], bf[ks], [&](int) {});

@@ -10,7 +10,8 @@
 // (eight waves);
 // schedule 2: ping-pong with A (K-contiguous) fetched in double-wide slabs,
 // so every A load instruction reads whole 128-byte lines: A in a ring of 3
-// double slabs, B in a ring of `stages` slabs (160 KiB for 256 x 256 x 32).
+// double slabs, B in a ring of `stages` slabs (160 KiB for 256 x 256 x 32);
+// B stored [N,K] (K-contiguous as well) in a ring of 2 double slabs.
 #pragma once
 
 #define GEMMEPI_TILES(X)         \

@@ -43,8 +43,10 @@ static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 2, 3, 1, 1, 1};
 // With B stored [N,K] both operands are K-contiguous; a 32-wide k slab then
 // fetches 64-byte row segments of both, which measured 0.83x on the
 // 65536 x 8192 x 16384 shape.  64-wide slabs fetch whole 128-byte lines and
-// lose nothing; schedule 2, which fetches A in 64-wide slabs, loses 0.98x
-// (its B rows stay 64-byte segments).
+// lose nothing.  Schedule 2 fetches both operands in 64-wide slabs; its
+// factor stays at the 0.98 the split-K constants were fitted with (at 1.0
+// the 2048 x 4096 x 11008 GEMM would be split twice over schedule 2, which
+// measured 0.97x of tile 7 unsplit).
 double tile_eff(int t, bool bt) {
   if (!bt || kTiles[t].bk >= 64) return kTileEff[t];
   return kTileEff[t] * (kTiles[t].sched == 2 ? 0.98 : 0.83);

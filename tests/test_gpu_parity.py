@@ -215,10 +215,10 @@ def _large(c, rows_count=4096):
     B = c.host_B()
     if c.epilogue in BGRAD_EPIS:
         ref = O.gemm_epilogue(c.host_A(), B, None, c.aux, c.M, c.N, c.K, c.dtype, c.epilogue,
-                              False, False, rows=rows)
+                              c.b_trans, c.bias_per_col, rows=rows)
     else:
         ref = O.gemm_epilogue(c.host_A(rows), B, c.bias[rows], None, len(rows), c.N, c.K,
-                              c.dtype, c.epilogue, False, False)
+                              c.dtype, c.epilogue, c.b_trans, c.bias_per_col)
     for flags in (0, ge.FLAG_UNFUSED):
         r = GpuRun(c, flags=flags)
         say("large", c.name, r.info)
@@ -240,6 +240,16 @@ def _large(c, rows_count=4096):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_config3_relu_aux_full(dtype):
     _large(wl.config3_relu_aux(dtype))
+
+
+def test_config3_relu_aux_full_b_stored_nk():
+    """C3's fp16 operands with B stored [N,K] (both operands K-contiguous,
+    so the 256 x 256 ping-pong tile also fetches B in double-wide slabs)."""
+    c = wl.config3_relu_aux("f16")
+    c.B_dev = c.B_dev.t().contiguous()
+    c.b_trans = True
+    c.name += "_bnk"
+    _large(c)
 
 
 def test_config4_drelu_bgrad_full():

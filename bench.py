@@ -59,6 +59,9 @@ def parse():
                     help="instead of the step: time the fused call, the library's plain GEMM "
                          "(epilogue DEFAULT) and torch.matmul (ROCm's BLAS) on the suite's GEMM "
                          "shapes, interleaved; one JSON line per shape")
+    ap.add_argument("--profile-layouts", action="store_true",
+                    help="only run the C3 fp16 fused kernel twice with B stored [K,N] (as the "
+                         "workload) and twice with the same B stored [N,K], for rocprofv3 --pmc runs")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only run the 1 GiB copy (calibration) and 16 decode calls each at "
                          "T = 1 and T = 16 over 16 rotated weight copies, for rocprofv3 --pmc runs")
@@ -353,6 +356,29 @@ def profile_traffic():
     log(f"profile-traffic done: {w.fused.info()}")
 
 
+def profile_layouts():
+    """C3's fp16 operands through the fused RELU_AUX_BIAS call, B as stored
+    by the workload ([K,N]) and the same B transposed to [N,K] (B_TRANS), two
+    launches each: the two B layouts of the same product side by side."""
+    import torch
+    import activation_epilogue_gemm_amd as ge
+    import workloads as wl
+    c = wl.config3_relu_aux("f16")
+    M, N, K = c.M, c.N, c.K
+    bias = upload_bits(c.bias, c.dtype, "cuda")
+    out = torch.empty(M, N, dtype=torch.float16, device="cuda")
+    aux = torch.empty(M, ge.aux_ld_words(N), dtype=torch.int32, device="cuda")
+    for bt in (False, True):
+        B = c.B_dev.t().contiguous() if bt else c.B_dev
+        with ge.plan(M, N, K, "f16", "RELU_AUX_BIAS", ge.FLAG_B_TRANS if bt else 0) as p:
+            for _ in range(2):
+                p.execute(c.A_dev, B, bias, aux, out)
+            torch.cuda.synchronize()
+            log(f"profile-layouts B {'[N,K]' if bt else '[K,N]'} done: {p.info()}")
+        del B
+        torch.cuda.empty_cache()
+
+
 def profile_decode():
     import torch
     import workloads as wl
@@ -466,12 +492,14 @@ def main():
         torch.cuda.set_device(0)
         compare_blas(args.only)
         return
-    if args.profile_traffic or args.profile_decode:
+    if args.profile_traffic or args.profile_decode or args.profile_layouts:
         import torch  # noqa: F401
         import activation_epilogue_gemm_amd as ge
         ge.library()
         if args.profile_traffic:
             profile_traffic()
+        elif args.profile_layouts:
+            profile_layouts()
         else:
             profile_decode()
         return

@@ -24,5 +24,5 @@ def test_help_lists_modes():
     r = run_bench("--help")
     assert r.returncode == 0
     for flag in ("--gpus", "--steps", "--warmup", "--compare-blas", "--profile-traffic",
-                 "--profile-decode", "--only"):
+                 "--profile-decode", "--profile-layouts", "--only"):
         assert flag in r.stdout

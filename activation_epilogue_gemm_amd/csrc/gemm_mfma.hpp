@@ -107,6 +107,53 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// G (1..4) loads of 16 bytes per lane from one buffer into G consecutive
+// 1 KiB LDS blocks starting at lds_addr, with a single write of M0: load g
+// carries the immediate offset 1024 g, which the hardware adds to both the
+// LDS and the global address, so voff[g] must be the global offset of block
+// g minus 1024 g (or an out-of-range offset, which reads zero).
+#ifndef GEMMEPI_M0_GROUPS
+#define GEMMEPI_M0_GROUPS 0
+#endif
+template <int G>
+__device__ __forceinline__ void buffer_load16_lds_group(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr,
+                                                        const uint32_t* voff) {
+  static_assert(G >= 1 && G <= 4, "one M0 covers at most 4 KiB of immediate offsets");
+  if constexpr (G == 1) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff[0]), "s"(r), "s"(lds_addr)
+                 : "memory");
+  } else if constexpr (G == 2) {
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "buffer_load_dwordx4 %0, %2, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen offset:1024 lds"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "s"(r), "s"(lds_addr)
+        : "memory");
+  } else if constexpr (G == 3) {
+    asm volatile(
+        "s_mov_b32 m0, %4\n\t"
+        "buffer_load_dwordx4 %0, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %3, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen offset:2048 lds"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "s"(r), "s"(lds_addr)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %5\n\t"
+        "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %4, 0 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %2, %4, 0 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %3, %4, 0 offen offset:3072 lds"
+        :
+        : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(r), "s"(lds_addr)
+        : "memory");
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const GEMMEPI_LDS void*)p;
 }
@@ -135,7 +182,10 @@ __device__ __forceinline__ f32x4 mfma_op(bf16x8 a, bf16x8 b, f32x4 c) {
 // the power limit), but in the kernel the higher clock comes with a lower
 // busy share: measured against the vendor BLAS on one box, C3 is unchanged,
 // C4 gains 3 % and the FFN up-projections lose 3-11 %, so 32x32x16 stays.
-constexpr int kMfma = 32;
+#ifndef GEMMEPI_MFMA_SHAPE
+#define GEMMEPI_MFMA_SHAPE 16
+#endif
+constexpr int kMfma = GEMMEPI_MFMA_SHAPE;
 constexpr int kAccN = kMfma * kMfma / 64;  // accumulator floats per lane per block
 constexpr int kLaneGroups = 64 / kMfma;    // lane groups l / kMfma
 constexpr int kKStep = 8 * kLaneGroups;    // k depth of one MFMA
@@ -529,16 +579,30 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     static_assert(!BPAIR || (B2_BYTES % (NT * 16) == 0 && NA * A2_BYTES + 2 * B2_BYTES <= SMEM_BYTES),
                   "B pair ring");
     static_assert(!BPAIR || A2_CH + B2_CH < 64, "vmcnt range");
-    uint32_t b2_off[BPAIR ? B2_CH : 1];
-    int b2_k[BPAIR ? B2_CH : 1];
+    // Each wave's loads of one slab (or pair) fill GS consecutive 1 KiB LDS
+    // blocks per M0 write (buffer_load16_lds_group): load j of the wave fills
+    // block wave * CH + j and carries the immediate offset 1024 (j % GS).  The
+    // descriptors start kShift bytes below the operand so that every offset
+    // stays non-negative: voff = global offset + kShift - 1024 (j % GS).
+    // (With GS = 1, load j fills block j * NW + wave, one M0 write per load.)
+    constexpr int GS_A = GEMMEPI_M0_GROUPS ? (A2_CH < 4 ? A2_CH : 4) : 1;
+    constexpr int GS_B = GEMMEPI_M0_GROUPS ? (G::B_CH < 4 ? G::B_CH : 4) : 1;
+    constexpr int GS_BP = GEMMEPI_M0_GROUPS ? (B2_CH < 4 ? B2_CH : 4) : 1;
+    static_assert(A2_CH % GS_A == 0 && G::B_CH % GS_B == 0 && (!BPAIR || B2_CH % GS_BP == 0),
+                  "load groups");
+    auto blk_of = [&](int j, int ch, int gs) { return gs > 1 ? wave * ch + j : j * NW + wave; };
+    constexpr uint32_t kShift = 3072;
+    uint32_t b2_off[B2_CH];
+    int b2_k[B2_CH];
     uint32_t b2_lds[2][KS];
     if constexpr (BPAIR) {
 #pragma unroll
       for (int i = 0; i < B2_CH; ++i) {
-        const int blk = i * NW + wave;
+        const int blk = blk_of(i, B2_CH, GS_BP);
         const int r = blk * RPB2 + lane / KCH2;
         const int kc = (lane % KCH2) ^ swz2(r);
-        b2_off[i] = (n0 + r < N) ? (uint32_t)((r * p.ldb + kc * 8) * 2) : kOOB;
+        b2_off[i] = (n0 + r < N) ? (uint32_t)((r * p.ldb + kc * 8) * 2) + kShift - 1024u * (i % GS_BP)
+                                 : kOOB;
         b2_k[i] = kc * 8;
       }
 #pragma unroll
@@ -550,41 +614,88 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           b2_lds[h][ks] = (uint32_t)(r * BK2 * 2 + ((chunk ^ swz2(r)) << 4));
         }
     }
+    // B stored [K,N] in single slabs: offsets of this wave's blocks, and
+    // which of them lie beyond K in the last slab
+    uint32_t bs_off[G::B_CH];
+    uint32_t bs_tail = 0;
+    if constexpr (!BPAIR) {
+#pragma unroll
+      for (int i = 0; i < G::B_CH; ++i) {
+        const int blk = blk_of(i, G::B_CH, GS_B);
+        const int kr = blk * G::B_RPB + lane / NCH;
+        const int nc = (lane % NCH) ^ G::swz_n(kr);
+        bs_off[i] = (n0 + nc * 8 < N) ? (uint32_t)((kr * p.ldb + nc * 8) * 2) + kShift - 1024u * (i % GS_B)
+                                      : kOOB;
+        if (k_last + kr >= K) bs_tail |= 1u << i;
+      }
+    }
     uint32_t a2_off[A2_CH];
     int a2_k[A2_CH];
 #pragma unroll
     for (int i = 0; i < A2_CH; ++i) {
-      const int blk = i * NW + wave;
+      const int blk = blk_of(i, A2_CH, GS_A);
       const int r = blk * RPB2 + lane / KCH2;
       const int kc = (lane % KCH2) ^ swz2(r);
-      a2_off[i] = (m0 + r < M) ? (uint32_t)((r * p.lda + kc * 8) * 2) : kOOB;
+      a2_off[i] = (m0 + r < M) ? (uint32_t)((r * p.lda + kc * 8) * 2) + kShift - 1024u * (i % GS_A) : kOOB;
       a2_k[i] = kc * 8;
     }
     const int k_stop = min(K, kt_end * BK);  // A columns at or past it read zero
-    auto issue_a2 = [&](int q, int stage, int j) {
+    // all loads of A pair q into A stage `stage`
+    auto issue_a2 = [&](int q, int stage) {
       const int slab0 = kt_begin + 2 * q;
       const bool none = slab0 >= kt_end;
       const int k0 = none ? 0 : slab0 * BK;
       const uint32_t st_addr =
           __builtin_amdgcn_readfirstlane(lds_addr_of(a_ring + stage * A2_BYTES));
-      const uint32_t kill = (none || k0 + a2_k[j] >= k_stop) ? kOOB : 0u;
-      const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (size_t)k0 * 2);
-      buffer_load16_lds(rA, st_addr + (j * NW + wave) * 1024, a2_off[j] | kill);
+      const __amdgpu_buffer_rsrc_t rA = make_rsrc(Abase + (size_t)k0 * 2 - kShift);
+      static_for<A2_CH / GS_A>([&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
+        uint32_t v[GS_A];
+#pragma unroll
+        for (int t = 0; t < GS_A; ++t) {
+          const int j = g * GS_A + t;
+          v[t] = (none || k0 + a2_k[j] >= k_stop) ? kOOB : a2_off[j];
+        }
+        buffer_load16_lds_group<GS_A>(rA, st_addr + blk_of(g * GS_A, A2_CH, GS_A) * 1024, v);
+      });
     };
-    auto issue_bp = [&](int q, int stage, int j) {
+    // all loads of B pair q (B stored [N,K]) into B pair stage `stage`
+    auto issue_bp = [&](int q, int stage) {
       const int slab0 = kt_begin + 2 * q;
       const bool none = slab0 >= kt_end;
       const int k0 = none ? 0 : slab0 * BK;
       const uint32_t st_addr =
           __builtin_amdgcn_readfirstlane(lds_addr_of(b_ring + stage * B2_BYTES));
-      const uint32_t kill = (none || k0 + b2_k[j] >= k_stop) ? kOOB : 0u;
-      const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + (size_t)k0 * 2);
-      buffer_load16_lds(rB, st_addr + (j * NW + wave) * 1024, b2_off[j] | kill);
+      const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + (size_t)k0 * 2 - kShift);
+      static_for<(BPAIR ? B2_CH : GS_BP) / GS_BP>([&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
+        uint32_t v[GS_BP];
+#pragma unroll
+        for (int t = 0; t < GS_BP; ++t) {
+          const int j = g * GS_BP + t;
+          v[t] = (none || k0 + b2_k[j] >= k_stop) ? kOOB : b2_off[j];
+        }
+        buffer_load16_lds_group<GS_BP>(rB, st_addr + blk_of(g * GS_BP, B2_CH, GS_BP) * 1024, v);
+      });
     };
-    // B slab kt into B stage `stage` through the schedule-1 loader (its B
-    // offsets are relative to a stage whose A part is A_BYTES long)
-    auto issue_b2 = [&](int kt, int stage, int j) {
-      issue_one(kt, b_ring + stage * G::B_BYTES - G::A_BYTES, G::A_CH + j);
+    // all loads of B slab kt (B stored [K,N]) into B stage `stage`
+    auto issue_b2 = [&](int kt, int stage) {
+      const bool none = kt >= kt_end;
+      const int k0 = none ? 0 : kt * BK;
+      const bool tail = kt == KT - 1;
+      const uint32_t st_addr =
+          __builtin_amdgcn_readfirstlane(lds_addr_of(b_ring + stage * G::B_BYTES));
+      const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bbase + (size_t)k0 * p.ldb * 2 - kShift);
+      static_for<(BPAIR ? GS_B : G::B_CH) / GS_B>([&](auto g_c) {
+        constexpr int g = decltype(g_c)::value;
+        uint32_t v[GS_B];
+#pragma unroll
+        for (int t = 0; t < GS_B; ++t) {
+          const int j = g * GS_B + t;
+          v[t] = (none || (tail && ((bs_tail >> j) & 1u))) ? kOOB : bs_off[j];
+        }
+        buffer_load16_lds_group<GS_B>(rB, st_addr + blk_of(g * GS_B, G::B_CH, GS_B) * 1024, v);
+      });
     };
     uint32_t a2_lds[2][KS];
 #pragma unroll
@@ -597,26 +708,18 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       }
     if constexpr (BPAIR) {
       // prologue: A pair 0, B pair 0, A pair 1; then wait for pair 0
-#pragma unroll
-      for (int j = 0; j < A2_CH; ++j) issue_a2(0, 0, j);
-#pragma unroll
-      for (int j = 0; j < B2_CH; ++j) issue_bp(0, 0, j);
-#pragma unroll
-      for (int j = 0; j < A2_CH; ++j) issue_a2(1, 1, j);
+      issue_a2(0, 0);
+      issue_bp(0, 0);
+      issue_a2(1, 1);
       wait_vmcnt<A2_CH>();
     } else {
     // prologue, in this order (the waits count on it): A pair 0, B slabs 0
     // and 1, A pair 1, B slab 2; then wait for slab 0
-#pragma unroll
-    for (int j = 0; j < A2_CH; ++j) issue_a2(0, 0, j);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + s2, s2, j);
-#pragma unroll
-    for (int j = 0; j < A2_CH; ++j) issue_a2(1, 1, j);
-#pragma unroll
-    for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + 2, 2, j);
+    issue_a2(0, 0);
+    issue_b2(kt_begin, 0);
+    issue_b2(kt_begin + 1, 1);
+    issue_a2(1, 1);
+    issue_b2(kt_begin + 2, 2);
     wait_vmcnt<G::B_CH + A2_CH + G::B_CH>();
     }
     __syncthreads();
@@ -662,21 +765,17 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           // only that A pair in flight, so B pair q + 1 and A pair q + 1
           // have landed before slab 2q + 2 is read.
           if constexpr (h == 0) {
-#pragma unroll
-            for (int j = 0; j < B2_CH; ++j) issue_bp(q + 1, (q + 1) & 1, j);
+            issue_bp(q + 1, (q + 1) & 1);
             wait_vmcnt<A2_CH + B2_CH>();
           } else {
-#pragma unroll
-            for (int j = 0; j < A2_CH; ++j) issue_a2(q + 2, a_next, j);
+            issue_a2(q + 2, a_next);
             wait_vmcnt<A2_CH>();
           }
         } else {
         if constexpr (h == 1) {
-#pragma unroll
-          for (int j = 0; j < A2_CH; ++j) issue_a2(q + 2, a_next, j);
+          issue_a2(q + 2, a_next);
         }
-#pragma unroll
-        for (int j = 0; j < G::B_CH; ++j) issue_b2(kt_begin + i + 3, (i + 3) & 3, j);
+        issue_b2(kt_begin + i + 3, (i + 3) & 3);
         wait_vmcnt<A2_CH + 2 * G::B_CH>();
         }
         phase_barrier();

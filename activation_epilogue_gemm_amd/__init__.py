@@ -107,8 +107,6 @@ def _load():
     lib.gemmepi_last_error.restype = ctypes.c_char_p
     lib.gemmepi_version.argtypes = []
     lib.gemmepi_version.restype = i32
-    lib.gemmepi_stream_read.argtypes = [vp, ctypes.c_size_t, vp, vp]
-    lib.gemmepi_stream_read.restype = ctypes.c_int
     lib.gemmepi_execute_norm.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
     lib.gemmepi_execute_norm.restype = ctypes.c_int
     lib.gemmepi_autotune.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(ctypes.c_float), vp]
@@ -151,13 +149,6 @@ def aux_ld_words(N: int) -> int:
 
 def aux_bytes(M: int, N: int) -> int:
     return int(_load().gemmepi_aux_bytes(int(M), int(N)))
-
-
-def stream_read(p, nbytes: int, sink, stream=None) -> None:
-    """gemmepi_stream_read: the reference 128-bit streaming read of `nbytes`
-    bytes at `p` (measurement helper)."""
-    st = _load().gemmepi_stream_read(_ptr(p), int(nbytes), _ptr(sink), _stream_handle(stream, p, sink))
-    _check(st, "gemmepi_stream_read")
 
 
 def _check(status: int, where: str):
@@ -247,11 +238,17 @@ class Plan:
         return int(_load().gemmepi_workspace_bytes(self._h))
 
     def _own_workspace(self, need: int, like):
-        """A zeroed workspace kept with the plan (memory plumbing only)."""
+        """A zeroed workspace kept with the plan (memory plumbing only).  The
+        zero fill runs on torch's current stream, which need not be the
+        stream the execution is enqueued on, so the fill is waited for here
+        (once per allocation): the arrival counters are zero before any
+        kernel on any stream can read them."""
         if self._ws is None or self._ws.numel() < need:
             import torch
             dev = like.device if hasattr(like, "device") else torch.device("cuda")
-            self._ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+            torch.cuda.current_stream(dev).synchronize()
+            self._ws = ws
         return self._ws
 
     def execute_norm(self, A: Pointer, B: Pointer, bias: Pointer, residual: Pointer,

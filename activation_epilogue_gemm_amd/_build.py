@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgemmepi.so")
+# measurement helpers used by the benchmark only, in a library of their own
+MEASURE_SOURCES = ["measure.hip"]
+MEASURE_LIB = os.path.join(PKG, "libgemmepi_measure.so")
 
 SOURCES = [
     "gemmepi_api.cpp",
@@ -78,8 +81,16 @@ def build(verbose: bool = True, jobs: int = 0, extra=()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
     os.replace(tmp, LIB)
+    mobjs = [_compile(src, extra) for src in MEASURE_SOURCES]
+    tmp = MEASURE_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *mobjs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, MEASURE_LIB)
     if verbose:
-        print(f"[gemmepi] built {LIB} in {time.time() - t0:.1f}s", file=sys.stderr)
+        print(f"[gemmepi] built {LIB} and {MEASURE_LIB} in {time.time() - t0:.1f}s",
+              file=sys.stderr)
     return LIB
 
 

@@ -255,25 +255,6 @@ __global__ void colsum_scalar_kernel(const T* dz, float* bgrad, int M, int N, in
   bgrad[n] = s;
 }
 
-// Reference read for the decode measurement: each workgroup reads one
-// contiguous 128 KiB block (16 loads of 16 bytes per thread, all in flight).
-constexpr int kStreamLoads = 16;
-__global__ void __launch_bounds__(512) stream_read_kernel(const u32x4* __restrict__ p, size_t n16,
-                                                          uint32_t* sink) {
-  const size_t base = (size_t)blockIdx.x * 512 * kStreamLoads + threadIdx.x;
-  u32x4 v[kStreamLoads];
-#pragma unroll
-  for (int u = 0; u < kStreamLoads; ++u) {
-    const size_t i = base + (size_t)u * 512;
-    v[u] = i < n16 ? p[i] : u32x4{0u, 0u, 0u, 0u};
-  }
-  uint32_t acc = 0;
-#pragma unroll
-  for (int u = 0; u < kStreamLoads; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  if (acc == 0x9E3779B9u) sink[blockIdx.x & 1023] = acc;
-}
-
-
 // out = round(out + residual), both [M, ldo]; the unfused path's residual
 // connection.
 template <typename T>
@@ -385,15 +366,6 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(T* out, const T* gamma, 
   }
 }
 }  // namespace
-
-hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s) {
-  const size_t n16 = bytes / 16;
-  const size_t per_block = 512 * (size_t)kStreamLoads;
-  const size_t blocks = (n16 + per_block - 1) / per_block;
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(512), 0, s, (const u32x4*)p, n16,
-                     sink);
-  return hipGetLastError();
-}
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, p, n, v);

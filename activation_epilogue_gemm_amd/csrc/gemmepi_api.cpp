@@ -773,21 +773,6 @@ const char* gemmepi_last_error(void) { return g_err.c_str(); }
 
 int32_t gemmepi_version(void) { return GEMMEPI_VERSION; }
 
-gemmepi_status_t gemmepi_stream_read(const void* p, size_t bytes, void* sink, void* stream) {
-  if (!p || !sink || bytes == 0)
-    return fail(GEMMEPI_ERR_INVALID_VALUE, "stream_read: null pointer or zero size");
-  if (!aligned(p, 16) || bytes % 16 != 0)
-    return fail(GEMMEPI_ERR_MISALIGNED, "stream_read: pointer and size must be 16-byte aligned");
-  if (bytes / (16 * 512 * 16) >= 0x7FFFFFFFull)
-    return fail(GEMMEPI_ERR_UNSUPPORTED, "stream_read: size too large");
-  gemmepi_status_t st = check_device();
-  if (st != GEMMEPI_OK) return st;
-  (void)hipGetLastError();
-  hipError_t e = launch_stream_read(p, bytes, (uint32_t*)sink, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "stream_read: %s", hipGetErrorString(e));
-  return GEMMEPI_OK;
-}
-
 gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
                                  void* aux, void* out, void* stream) {
   if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: null plan");

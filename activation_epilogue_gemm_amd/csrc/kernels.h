@@ -99,7 +99,6 @@ hipError_t launch_mask_apply(int dtype, void* out, const uint32_t* aux, int M, i
 // out = out * gelu'(z), z the saved pre-activation [M, ldo] (unfused DGELU)
 hipError_t launch_dgelu_apply(int dtype, void* out, const void* z, int M, int N, int ldo,
                               hipStream_t s);
-hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_colsum(int dtype, const void* dz, float* bgrad, int M, int N, int ldo,
                          hipStream_t s);
 // out += residual (both [M, ldo]), rounded to the dtype

@@ -68,6 +68,58 @@ def parse():
     return ap.parse_args()
 
 
+MEASURE_LIB = os.path.join(ROOT, "activation_epilogue_gemm_amd", "libgemmepi_measure.so")
+_measure = None
+
+
+def measure_library():
+    """libgemmepi_measure (the stream-read reference), built beside libgemmepi."""
+    global _measure
+    if _measure is None:
+        import ctypes
+        if not os.path.exists(MEASURE_LIB):
+            raise RuntimeError(f"{MEASURE_LIB} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(MEASURE_LIB)
+        vp = ctypes.c_void_p
+        lib.gemmepi_measure_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int,
+                                                    ctypes.c_int, ctypes.c_int, vp]
+        lib.gemmepi_measure_stream_read.restype = ctypes.c_int
+        _measure = lib
+    return _measure
+
+
+def stream_read(buf, nbytes, sink, threads=512, loads=16, nontemporal=0):
+    """One 128-bit streaming read of the first `nbytes` bytes of `buf`
+    (a device tensor) on torch's current stream."""
+    import torch
+    st = measure_library().gemmepi_measure_stream_read(
+        buf.data_ptr(), int(nbytes), sink.data_ptr(), int(threads), int(loads), int(nontemporal),
+        torch.cuda.current_stream(buf.device).cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"gemmepi_measure_stream_read failed with status {st}")
+
+
+# launch shapes of the stream-read sweep: (threads, loads per thread, non-temporal)
+STREAM_SHAPES = [(t, l, nt) for t in (256, 512, 1024) for l in (4, 8, 16, 32) for nt in (0, 1)]
+
+
+def sweep_stream_read(bufs, nbytes, reps, stream, shapes=None):
+    """Time every launch shape of the stream read over the rotated buffers
+    (each read cold from HBM); returns {shape: ms per read}, medians of 5
+    trials."""
+    import statistics
+    import torch
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    res = {}
+    for shp in shapes or STREAM_SHAPES:
+        t, l, nt = shp
+        fn = lambda i: stream_read(bufs[i % len(bufs)], nbytes, sink, t, l, nt)  # noqa: E731
+        for i in range(2):
+            fn(i)
+        res[shp] = statistics.median(time_region(fn, reps, stream) for _ in range(5))
+    return res
+
+
 def torch_dtype(dtype):
     import torch
     return torch.float16 if dtype == "f16" else torch.bfloat16
@@ -563,6 +615,7 @@ def main():
 
     # per-workload fused / unfused timing
     per = {}
+    stream_ref = None
     for w in suite + extras:
         reps = args.reps
         if not reps:
@@ -579,16 +632,26 @@ def main():
             entry.update({"in_step": False, "gbs_algorithmic": round(w.bytes / f_ms / 1e6, 1)})
         if w.name.startswith("c1_"):
             gbs = w.bytes / f_ms / 1e6
-            # the practical floor: a plain 128-bit read of the same weight bytes,
-            # rotated over the same copies, launched the same way
-            sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+            # the practical floor: the fastest launch shape of a plain 128-bit
+            # read of the same weight bytes, rotated over the same copies
             wb = w.B.numel() * 2
-            rot = w.rotation
-            s_ms = time_region(lambda i: ge.stream_read(rot[i % len(rot)][1], wb, sink), reps, stream)
+            if stream_ref is None:
+                sweep = sweep_stream_read([r[1] for r in w.rotation], wb, reps, stream)
+                best = min(sweep, key=sweep.get)
+                stream_ref = {"ms": sweep[best], "shape": best,
+                              "sweep_gbs": {f"{t}x{l}{'nt' if nt else ''}": round(wb / v / 1e6, 1)
+                                            for (t, l, nt), v in sweep.items()}}
+                log(f"stream-read sweep over {wb} bytes: best {best} "
+                    f"{wb / stream_ref['ms'] / 1e6:.1f} GB/s; {stream_ref['sweep_gbs']}")
+            s_ms = stream_ref["ms"]
+            t, l, nt = stream_ref["shape"]
             entry.update({"gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_GBS, 4),
                           "bytes": w.bytes, "stream_read_ms": round(s_ms, 5),
                           "stream_read_gbs": round(wb / s_ms / 1e6, 1),
+                          "stream_read_shape": f"{t} threads x {l} loads{' non-temporal' if nt else ''}",
                           "frac_of_stream_read": round(s_ms / f_ms, 4)})
+            if w.name == "c1_decode_T1":
+                entry["stream_read_sweep_gbs"] = stream_ref["sweep_gbs"]
         per[w.name] = entry
         log(f"{w.name}: fused {f_ms:.4f} ms unfused {u_ms:.4f} ms "
             f"x{u_ms / f_ms:.3f} {entry['tflops']} TFLOP/s" +

@@ -334,20 +334,6 @@ const char* gemmepi_last_error(void);
 /* GEMMEPI_VERSION of the built library. */
 int32_t gemmepi_version(void);
 
-/*
- * Measurement helper, not part of the GEMM: read `bytes` bytes at `p` once
- * with 128-bit loads spread over the whole GPU (128 KiB per workgroup) and
- * write at most one word per workgroup into `sink` so the reads cannot be
- * dropped.  It is the practical HBM read rate that the thin-M decode kernel,
- * which must stream its whole weight matrix on every call (ops-nn MatMul
- * fusion article, section "Why MatMul is the core bottleneck of LLM
- * inference"), is compared against.
- *   p      device memory, 16-byte aligned; bytes a multiple of 16
- *   sink   device memory of at least 4096 bytes (contents unspecified)
- *   stream hipStream_t or NULL; the call only enqueues
- * Errors: INVALID_VALUE (null pointer, bytes 0), MISALIGNED, HIP.
- */
-gemmepi_status_t gemmepi_stream_read(const void* p, size_t bytes, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

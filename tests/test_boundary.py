@@ -24,7 +24,7 @@ def test_header_declares_the_api():
     for n in ("gemmepi_plan", "gemmepi_plan_tiled", "gemmepi_execute", "gemmepi_plan_destroy",
               "gemmepi_plan_info", "gemmepi_aux_ld_words", "gemmepi_aux_bytes",
               "gemmepi_status_string", "gemmepi_last_error", "gemmepi_num_tiles",
-              "gemmepi_tile_name", "gemmepi_version", "gemmepi_stream_read",
+              "gemmepi_tile_name", "gemmepi_version",
               "gemmepi_execute_norm", "gemmepi_norm_stats_bytes", "gemmepi_autotune"):
         assert n in names
 
@@ -58,9 +58,10 @@ def test_plan_validation():
     assert _plan_status(64, 64, 64, flags=1 << 9) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 64, tile=ge.num_tiles()) == ge.ERR_INVALID_VALUE
     assert _plan_status(64, 64, 60) == ge.ERR_MISALIGNED          # K % 8
+    assert "K=60" in ge.last_error()
     assert _plan_status(64, 60, 64) == ge.ERR_MISALIGNED          # N % 8 without B_TRANS
+    assert "N=60" in ge.last_error()
     assert _plan_status(64, 60, 64, flags=ge.FLAG_B_TRANS) == ge.OK
-    assert "K=60" in ge.last_error() or True
     lib = ge.library()
     assert lib.gemmepi_plan(None, 1, 1, 8, 0, 0, 0) == ge.ERR_INVALID_VALUE
 
@@ -147,9 +148,19 @@ def test_execute_rejects_bad_pointers_before_any_hip_call():
         assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, None, 4096, None) == ge.ERR_INVALID_VALUE
         assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, 4104, 4096, None) == ge.ERR_MISALIGNED
     assert lib.gemmepi_execute(None, 4096, 4096, 4096, 4096, 4096, None) == ge.ERR_INVALID_VALUE
-    assert lib.gemmepi_stream_read(None, 4096, 4096, None) == ge.ERR_INVALID_VALUE
-    assert lib.gemmepi_stream_read(4096, 0, 4096, None) == ge.ERR_INVALID_VALUE
-    assert lib.gemmepi_stream_read(4100, 4096, 4096, None) == ge.ERR_MISALIGNED
+
+
+def test_measurement_helper_is_outside_the_gemm_library():
+    """The stream-read reference of the benchmark lives in its own library;
+    it validates its arguments before any HIP call."""
+    import bench
+    assert not hasattr(ge.library(), "gemmepi_stream_read")
+    m = bench.measure_library()
+    assert m.gemmepi_measure_stream_read(None, 4096, 4096, 512, 16, 0, None) == 1
+    assert m.gemmepi_measure_stream_read(4096, 0, 4096, 512, 16, 0, None) == 1
+    assert m.gemmepi_measure_stream_read(4100, 4096, 4096, 512, 16, 0, None) == 1
+    assert m.gemmepi_measure_stream_read(4096, 4096, 4096, 384, 16, 0, None) == 1
+    assert m.gemmepi_measure_stream_read(4096, 4096, 4096, 512, 12, 0, None) == 1
 
 
 def test_binding_checks_tensor_arguments():

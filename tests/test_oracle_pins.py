@@ -64,6 +64,24 @@ def test_worked_example_all_epilogues():
     assert r.bgrad.tolist() == ex["DRELU_BGRAD_bgrad"]
 
 
+def test_relu_and_mask_at_exact_zero():
+    """ReLU passes z only where z > 0 (Y = ReLU(WX + B)), and the aux mask
+    records where it passed, so an exactly zero pre-activation gives output 0
+    and mask bit 0.  Hand-worked, M = 1, K = 2, N = 4:
+      A = [1, 2];  B columns (1, -0.5), (-1, 0.5), (3, -1), (2, -1)
+      acc = [1 - 1, -1 + 1, 3 - 2, 2 - 2] = [0, 0, 1, 0]
+    bias 0:  out = [0, 0, 1, 0], mask word = bit 2 = 4;
+    bias -1: z = [-1, -1, 0, -1], out = 0, mask word = 0."""
+    A = _f16([1.0, 2.0])
+    B = _f16([[1.0, -1.0, 3.0, 2.0], [-0.5, 0.5, -1.0, -1.0]])
+    for b, want_out, want_word in ((0.0, [0.0, 0.0, 1.0, 0.0], 4), (-1.0, [0.0] * 4, 0)):
+        for epi in ("RELU_BIAS", "RELU_AUX_BIAS"):
+            r = O.gemm_epilogue(A, B, _f16([b]), None, 1, 4, 2, "f16", epi, False, False)
+            assert O.decode_f16(r.out).tolist() == [want_out]
+            if epi == "RELU_AUX_BIAS":
+                assert r.mask[0].tolist() == [want_word, 0, 0, 0]
+
+
 # ---------------------------------------------------------------- brute force
 BRUTE_SHAPES = [(1, 1, 1), (3, 5, 8), (7, 6, 5), (8, 8, 8), (5, 33, 4), (2, 65, 3)]
 

@@ -111,6 +111,10 @@ def _load():
     lib.gemmepi_execute_norm.restype = ctypes.c_int
     lib.gemmepi_autotune.argtypes = [vp, vp, vp, vp, vp, vp, i32, ctypes.POINTER(ctypes.c_float), vp]
     lib.gemmepi_autotune.restype = ctypes.c_int
+    lib.gemmepi_execute_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.gemmepi_execute_noalloc.restype = ctypes.c_int
+    lib.gemmepi_noalloc_scratch_bytes.argtypes = []
+    lib.gemmepi_noalloc_scratch_bytes.restype = ctypes.c_size_t
     lib.gemmepi_norm_stats_bytes.argtypes = [i64]
     lib.gemmepi_norm_stats_bytes.restype = ctypes.c_size_t
     _lib = lib
@@ -231,6 +235,20 @@ class Plan:
                                         _ptr(out), _ptr(workspace), int(nbytes),
                                         _stream_handle(stream, A, B, out))
         _check(st, "gemmepi_execute_ws")
+
+    def execute_noalloc(self, A: Pointer, B: Pointer, bias: Pointer = None, aux: Pointer = None,
+                        out: Pointer = None, stream=None, check: bool = True) -> None:
+        """Enqueue one execution through gemmepi_execute_noalloc: a split-K
+        plan uses the library's static device scratch instead of a
+        workspace, so nothing is allocated.  Calls that overlap on one device
+        race on that scratch."""
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        if check:
+            self._check_tensors(A, B, bias, aux, out)
+        st = _load().gemmepi_execute_noalloc(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(aux),
+                                             _ptr(out), _stream_handle(stream, A, B, out))
+        _check(st, "gemmepi_execute_noalloc")
 
     def workspace_bytes(self) -> int:
         """gemmepi_workspace_bytes: device workspace this plan needs (0 unless
@@ -380,6 +398,11 @@ class Plan:
             raise ValueError(f"operands on several devices: {devs}")
         if devs and next(iter(devs)).type != "cuda":
             raise ValueError("operands are not on the GPU; libgemmepi needs GPU (HIP) memory")
+
+
+def noalloc_scratch_bytes() -> int:
+    """gemmepi_noalloc_scratch_bytes: the per-device static scratch size."""
+    return int(_load().gemmepi_noalloc_scratch_bytes())
 
 
 def norm_stats_bytes(M: int) -> int:

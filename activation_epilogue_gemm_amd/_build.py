@@ -27,6 +27,7 @@ SOURCES = [
     "gemmepi_api.cpp",
     "elementwise.hip",
     "decode.hip",
+    "noalloc.hip",
     "gemm_f16_bn.hip",
     "gemm_f16_bt.hip",
     "gemm_bf16_bn.hip",

@@ -499,8 +499,13 @@ bool plan_live(gemmepi_plan_t plan) {
   return false;
 }
 
+// ws_static: the workspace is the library's static scratch (ws is its
+// address on the current device): it is not checked as a caller allocation,
+// and its counters are cleared here, since the previous call's contents
+// remain in it.
 gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void* B, void* bias,
-                              void* aux, void* out, void* ws, size_t ws_bytes, void* stream) {
+                              void* aux, void* out, void* ws, size_t ws_bytes, void* stream,
+                              bool ws_static = false) {
   const int epi = p.epi;
   const bool bt = p.flags & GEMMEPI_FLAG_B_TRANS;
   const bool per_col = p.flags & GEMMEPI_FLAG_BIAS_PER_COL;
@@ -544,7 +549,8 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
     if ((st = check_device_ptr(out, "out")) != GEMMEPI_OK) return st;
     if (needs_bias && (st = check_device_ptr(bias, "bias")) != GEMMEPI_OK) return st;
     if (needs_aux && (st = check_device_ptr(aux, "aux")) != GEMMEPI_OK) return st;
-    if (ws_need > 0 && (st = check_device_ptr(ws, "workspace")) != GEMMEPI_OK) return st;
+    if (ws_need > 0 && !ws_static && (st = check_device_ptr(ws, "workspace")) != GEMMEPI_OK)
+      return st;
   }
 
   hipStream_t s = (hipStream_t)stream;
@@ -554,6 +560,12 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
   hipError_t e = hipSuccess;
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
 
+  if (ws_need > 0 && ws_static) {
+    // a fill kernel rather than hipMemsetAsync, so a captured stream
+    // replays it correctly
+    e = launch_fill_f32((float*)ws, (int64_t)(counter_bytes(p) / 4), 0.0f, s);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "scratch counter fill: %s", hipGetErrorString(e));
+  }
   if (bgrad_epi) {
     e = launch_fill_f32((float*)bias, N, 0.0f, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "bgrad fill: %s", hipGetErrorString(e));
@@ -650,6 +662,27 @@ gemmepi_status_t gemmepi_execute_ws(gemmepi_plan_t plan, const void* A, const vo
   if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: null plan");
   return execute_impl(*plan, A, B, bias, aux, out, workspace, workspace_bytes, stream);
 }
+
+gemmepi_status_t gemmepi_execute_noalloc(gemmepi_plan_t plan, const void* A, const void* B,
+                                         void* bias, void* aux, void* out, void* stream) {
+  if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "execute_noalloc: null plan");
+  const size_t need = workspace_bytes(*plan);
+  if (need == 0) return execute_impl(*plan, A, B, bias, aux, out, nullptr, 0, stream);
+  if (need > kScratchBytes)
+    return fail(GEMMEPI_ERR_UNSUPPORTED,
+                "execute_noalloc: the plan's split-K workspace is %zu bytes, more than the "
+                "library's static scratch of %zu bytes (use gemmepi_execute_ws)",
+                need, kScratchBytes);
+  gemmepi_status_t st = check_device();
+  if (st != GEMMEPI_OK) return st;
+  void* ws = nullptr;
+  const hipError_t e = scratch_pointer(&ws);
+  if (e != hipSuccess)
+    return fail(GEMMEPI_ERR_HIP, "execute_noalloc: static scratch address: %s", hipGetErrorString(e));
+  return execute_impl(*plan, A, B, bias, aux, out, ws, kScratchBytes, stream, true);
+}
+
+size_t gemmepi_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const void* B,
                                       const void* bias, const void* residual,

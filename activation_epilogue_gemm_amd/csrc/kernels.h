@@ -110,6 +110,12 @@ hipError_t launch_norm_rows(int dtype, void* out, const void* gamma, const void*
                             double* stats, int M, int N, int ldo, float eps, int layernorm,
                             int from_stats, hipStream_t s);
 
+// The library's static device scratch (noalloc.hip): kScratchBytes per
+// device, for the split-K workspace of gemmepi_execute_noalloc.  Returns the
+// current device's address of it (looked up once per device).
+constexpr size_t kScratchBytes = (size_t)48 << 20;
+hipError_t scratch_pointer(void** ptr);
+
 // per-dtype launcher tables filled by each instantiation file
 using GemmLauncher = hipError_t (*)(const GemmArgs&, hipStream_t);
 hipError_t launch_gemm_f16_bn(int tile, const GemmArgs& a, hipStream_t s);

@@ -25,7 +25,9 @@
  *     which is the x.W^T orientation of a linear layer with W stored
  *     [out,in].  out is [M,N].
  *   - Device pointers are HIP device pointers on the current device; the
- *     caller owns every buffer.  The library never allocates device memory.
+ *     caller owns every buffer.  The library never allocates device memory
+ *     at run time; its only device memory is the static scratch of
+ *     gemmepi_execute_noalloc, allocated by the code-object loader.
  *   - Every call returns a status and never aborts or prints;
  *     gemmepi_last_error() returns a thread-local description of the last
  *     failure.
@@ -238,6 +240,33 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
 gemmepi_status_t gemmepi_execute_ws(gemmepi_plan_t plan, const void* A, const void* B, void* bias,
                                     void* aux, void* out, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * gemmepi_execute_ws, but a plan that splits K takes its workspace from a
+ * static device array of the library, gemmepi_noalloc_scratch_bytes()
+ * bytes (48 MiB) per device, which the code-object loader allocates when
+ * the library's kernels are first loaded on a device and which stays
+ * allocated until the process ends.  The call itself allocates nothing.
+ * Its arrival counters are cleared by a fill kernel at the start of each
+ * call (the array keeps the previous call's contents).  For a plan that
+ * does not split K it is identical to gemmepi_execute.
+ *
+ * Every call on one device shares that device's array: calls that may
+ * overlap on one device (other streams, other threads) race on it and
+ * give wrong results; serialise them, or give each its own workspace
+ * through gemmepi_execute_ws.
+ *
+ * Arguments as gemmepi_execute.  Errors: as gemmepi_execute, plus
+ * UNSUPPORTED when the plan's workspace (gemmepi_workspace_bytes) exceeds
+ * the static array, HIP when its device address cannot be looked up.
+ */
+gemmepi_status_t gemmepi_execute_noalloc(gemmepi_plan_t plan, const void* A, const void* B,
+                                         void* bias, void* aux, void* out, void* stream);
+
+/* Size in bytes of the per-device static scratch of gemmepi_execute_noalloc. */
+size_t gemmepi_noalloc_scratch_bytes(void);
 
 /*
  * Measured tile choice for a tiled-GEMM plan: the pages' planner "tries

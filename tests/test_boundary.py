@@ -24,7 +24,7 @@ def test_header_declares_the_api():
     for n in ("gemmepi_plan", "gemmepi_plan_tiled", "gemmepi_execute", "gemmepi_plan_destroy",
               "gemmepi_plan_info", "gemmepi_aux_ld_words", "gemmepi_aux_bytes",
               "gemmepi_status_string", "gemmepi_last_error", "gemmepi_num_tiles",
-              "gemmepi_tile_name", "gemmepi_version",
+              "gemmepi_tile_name", "gemmepi_version", "gemmepi_execute_noalloc",
               "gemmepi_execute_norm", "gemmepi_norm_stats_bytes", "gemmepi_autotune"):
         assert n in names
 
@@ -148,6 +148,8 @@ def test_execute_rejects_bad_pointers_before_any_hip_call():
         assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, None, 4096, None) == ge.ERR_INVALID_VALUE
         assert lib.gemmepi_execute(p._h, 4096, 4096, 4096, 4104, 4096, None) == ge.ERR_MISALIGNED
     assert lib.gemmepi_execute(None, 4096, 4096, 4096, 4096, 4096, None) == ge.ERR_INVALID_VALUE
+    assert lib.gemmepi_execute_noalloc(None, 4096, 4096, 4096, 4096, 4096, None) == \
+        ge.ERR_INVALID_VALUE
 
 
 def test_measurement_helper_is_outside_the_gemm_library():

@@ -49,6 +49,7 @@ FLAG_UNFUSED = 1 << 2
 FLAG_VALIDATE = 1 << 3
 FLAG_NO_DECODE = 1 << 4
 FLAG_SPLIT_K = 1 << 5
+FLAG_STAGE_B = 1 << 6
 
 
 class GemmEpiError(RuntimeError):

@@ -255,6 +255,45 @@ __global__ void colsum_scalar_kernel(const T* dz, float* bgrad, int M, int N, in
   bgrad[n] = s;
 }
 
+// dst[n, k] = src[k, n]: a [K, N] matrix of 16-bit elements (N contiguous)
+// copied to [N, K] (K contiguous), so that the tiled GEMM can read B with
+// K-contiguous slabs.  One 64 x 64 tile per workgroup: 16-byte loads along
+// n into LDS rows of k (padded by 16 bytes, so that the column gathers of
+// the write-out hit distinct banks), then 16-byte stores along k.  K and N
+// are multiples of 8, so no 16-byte chunk straddles an edge.
+constexpr int kTr = 64;
+constexpr int kTrPad = kTr + 8;  // LDS row pitch in elements
+__global__ void __launch_bounds__(256) transpose16_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ dst, int K, int N,
+                                                          int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTr][kTrPad];  // [k][n]
+  const int tk = blockIdx.x / tiles_n, tn = blockIdx.x - tk * tiles_n;
+  const int k0 = tk * kTr, n0 = tn * kTr;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = t + 256 * j;
+    const int kr = c >> 3, cc = c & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + kr < K && n0 + cc * 8 < N)
+      v = *(const u32x4*)(src + (size_t)(k0 + kr) * N + n0 + cc * 8);
+    *(u32x4*)&tile[kr][cc * 8] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = t + 256 * j;
+    const int nr = c >> 3, kc = c & 7;
+    if (n0 + nr >= N || k0 + kc * 8 >= K) continue;
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = tile[kc * 8 + i][nr];
+    const u32x4 w = {e[0] | (uint32_t)e[1] << 16, e[2] | (uint32_t)e[3] << 16,
+                     e[4] | (uint32_t)e[5] << 16, e[6] | (uint32_t)e[7] << 16};
+    *(u32x4*)(dst + (size_t)(n0 + nr) * K + k0 + kc * 8) = w;
+  }
+}
+
 // out = round(out + residual), both [M, ldo]; the unfused path's residual
 // connection.
 template <typename T>
@@ -366,6 +405,16 @@ __global__ void __launch_bounds__(256) norm_rows_kernel(T* out, const T* gamma, 
   }
 }
 }  // namespace
+
+hipError_t launch_transpose16(const void* src, void* dst, int K, int N, hipStream_t s) {
+  if (K < 1 || N < 1 || K % 8 || N % 8) return hipErrorInvalidValue;
+  const int tiles_k = (K + kTr - 1) / kTr, tiles_n = (N + kTr - 1) / kTr;
+  const int64_t blocks = (int64_t)tiles_k * tiles_n;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const uint16_t*)src, (uint16_t*)dst, K, N, tiles_n);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n, kThreads)), dim3(kThreads), 0, s, p, n, v);

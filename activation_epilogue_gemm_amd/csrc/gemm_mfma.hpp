@@ -25,14 +25,16 @@
 //   * LDS rows are XOR-swizzled in 16-byte units so that the 128-bit
 //     fragment reads (and the 64-bit transposing reads of a row-major [K,N]
 //     B) hit distinct banks of the 64-bank LDS;
-//   * v_mfma_f32_32x32x16_{f16,bf16} (kMfma below): exact products, fp32
+//   * v_mfma_f32_16x16x32_{f16,bf16} or v_mfma_f32_32x32x16_{f16,bf16}
+//     (the tile's MFMA shape MT, MfmaShape below): exact products, fp32
 //     accumulation.  The B fragment is passed as the instruction's first
 //     operand and the A fragment as its second, so the accumulator holds the
-//     transposed block: lane l, element r of a 32x32 block is
+//     transposed block: with MT = 16 lane l, element r of a 16x16 block is
+//         row m = l % 16,   column n = 4*(l/16) + r,
+//     with MT = 32 lane l, element r of a 32x32 block is
 //         row m = l % 32,   column n = 8*(r/4) + 4*(l/32) + (r%4),
-//     i.e. each lane owns one output row and 4 runs of 4 consecutive
-//     columns, which become 8-byte stores.  (With kMfma = 16, the 16x16x32
-//     form: row l % 16, columns 4*(l/16) + r.)
+//     i.e. each lane owns one output row and runs of 4 consecutive columns,
+//     which become 8-byte stores.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -73,6 +75,30 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Debug build (GEMMEPI_LDS_POISON=1), a race detector for the LDS rings:
+// before a wave issues a global->LDS load, it fills the 1 KiB block that
+// load will write with NaN bits (0xFFFF in fp16 and in bf16) and waits for
+// those writes.  A wave that reads a block before the load into it has
+// landed (a missing vmcnt wait or barrier) then reads NaN rather than the
+// block's previous, plausible contents, and a refill that overtakes a
+// reader of the previous contents hands it NaN as well; after the main loop
+// the whole ring is poisoned again before the epilogue reuses it.  On
+// integer inputs every such read turns the result wrong, where the release
+// build would often compute the right result from stale data.
+#ifndef GEMMEPI_LDS_POISON
+#define GEMMEPI_LDS_POISON 0
+#endif
+
+__device__ __forceinline__ void poison_lds_blocks(uint32_t lds_addr, int blocks) {
+  if constexpr (GEMMEPI_LDS_POISON != 0) {
+    const u32x4 nan4 = {~0u, ~0u, ~0u, ~0u};
+    for (int b = 0; b < blocks; ++b)
+      *(GEMMEPI_LDS u32x4*)(GEMMEPI_LDS uint8_t*)(uintptr_t)(lds_addr + 1024u * b +
+                                                             16u * (threadIdx.x & 63u)) = nan4;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 // 16 bytes per lane from a buffer straight into LDS: lane L's data lands at
 // LDS byte address lds_addr + 16 L (lds_addr must be wave-uniform; it goes
 // to M0).  Written as inline assembly on purpose: the compiler then does not
@@ -82,6 +108,7 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 // barrier before any wave reads the stage.
 __device__ __forceinline__ void buffer_load16_lds(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr,
                                                   uint32_t off) {
+  poison_lds_blocks(lds_addr, 1);
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(off), "s"(r), "s"(lds_addr)
@@ -119,6 +146,7 @@ template <int G>
 __device__ __forceinline__ void buffer_load16_lds_group(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr,
                                                         const uint32_t* voff) {
   static_assert(G >= 1 && G <= 4, "one M0 covers at most 4 KiB of immediate offsets");
+  poison_lds_blocks(lds_addr, G);
   if constexpr (G == 1) {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                  :
@@ -175,25 +203,25 @@ __device__ __forceinline__ f32x4 mfma_op(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The GEMM's MFMA shape: kMfma x kMfma output blocks, v_mfma_f32_32x32x16
-// (kMfma = 32) or v_mfma_f32_16x16x32 (kMfma = 16); every part of the kernel
-// is written for both.  The 16x16x32 form spends less energy per FLOP (in a
-// bare MFMA loop shaped like this kernel's it holds a ~14 % higher clock at
-// the power limit), but in the kernel the higher clock comes with a lower
-// busy share: measured against the vendor BLAS on one box, C3 is unchanged,
-// C4 gains 3 % and the FFN up-projections lose 3-11 %, so 32x32x16 stays.
-#ifndef GEMMEPI_MFMA_SHAPE
-#define GEMMEPI_MFMA_SHAPE 16
-#endif
-constexpr int kMfma = GEMMEPI_MFMA_SHAPE;
-constexpr int kAccN = kMfma * kMfma / 64;  // accumulator floats per lane per block
-constexpr int kLaneGroups = 64 / kMfma;    // lane groups l / kMfma
-constexpr int kKStep = 8 * kLaneGroups;    // k depth of one MFMA
-constexpr int kColStride = 4 * kLaneGroups;  // columns between a lane's 4-column groups
+// The MFMA shape of a tile: MT x MT output blocks, v_mfma_f32_32x32x16
+// (MT = 32) or v_mfma_f32_16x16x32 (MT = 16); every part of the kernel is
+// written for both, and the tile table picks one per tile.  The 16x16x32
+// form spends less energy per FLOP (in a bare MFMA loop shaped like the
+// 256 x 256 tile it holds a ~14 % higher clock at the power limit); measured
+// interleaved on one box against 32x32x16 it ran the large tiles 1-11 %
+// faster and the 64 x 64 tile of the 1024 x 512 x 2048 GEMM 6 % slower.
 template <int MT> struct AccOf;
 template <> struct AccOf<32> { using type = f32x16; };
 template <> struct AccOf<16> { using type = f32x4; };
-using AccBlock = typename AccOf<kMfma>::type;
+template <int MT>
+struct MfmaShape {
+  static_assert(MT == 16 || MT == 32, "MFMA shape");
+  static constexpr int kAccN = MT * MT / 64;       // accumulator floats per lane per block
+  static constexpr int kLaneGroups = 64 / MT;      // lane groups l / MT
+  static constexpr int kKStep = 8 * kLaneGroups;   // k depth of one MFMA
+  static constexpr int kColStride = 4 * kLaneGroups;  // columns between a lane's 4-column groups
+  using AccBlock = typename AccOf<MT>::type;
+};
 
 // 4 consecutive-k values of one column from a row-major [K,N] LDS tile:
 // within each group of 16 lanes, lane (4*h + q) points at row h, columns
@@ -300,8 +328,9 @@ __device__ __forceinline__ void tile_coords(const GemmArgs& p, int bid, int nb, 
   tn = r / gsz;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int NS>
+template <int BM, int BN, int BK, int WM, int WN, int NS, int MT>
 struct GemmTile {
+  static constexpr int kMfma = MT;
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -359,9 +388,13 @@ __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT, int SCHED>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT, int SCHED, int MT>
 __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p) {
-  using G = GemmTile<BM, BN, BK, WM, WN, NS>;
+  using G = GemmTile<BM, BN, BK, WM, WN, NS, MT>;
+  using Shape = MfmaShape<MT>;
+  constexpr int kMfma = MT;
+  constexpr int kAccN = Shape::kAccN, kKStep = Shape::kKStep, kColStride = Shape::kColStride;
+  using AccBlock = typename Shape::AccBlock;
   using V8 = typename Frag<T>::type;
   constexpr int NT = G::NT, NW = G::NW, WTM = G::WTM, WTN = G::WTN, FM = G::FM, FN = G::FN;
   constexpr int KCH = G::KCH, NCH = G::NCH, A_CH = G::A_CH, B_CH = G::B_CH;
@@ -518,16 +551,31 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     }
   };
 
-  // the FM x FN MFMAs of one k step; between(q) is placed after MFMA q
-  auto mfma_step = [&](const V8 (&af)[FM], const V8 (&bf)[FN], auto&& between) {
+  // MFMAs [lo, hi) of a slab's KS x FM x FN (k step major), on registers;
+  // between(q) is placed after MFMA q
+  auto mfma_range_with = [&](const V8 (&af)[KS][FM], const V8 (&bf)[KS][FN], int lo, int hi,
+                             auto&& between) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        acc[fm][fn] = mfma_op(bf[fn], af[fm], acc[fm][fn]);
-        between(fm * FN + fn);
-      }
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const int q = (ks * FM + fm) * FN + fn;
+          if (q >= lo && q < hi) {
+            acc[fm][fn] = mfma_op(bf[ks][fn], af[ks][fm], acc[fm][fn]);
+            between(q);
+          }
+        }
   };
+  auto mfma_range = [&](const V8 (&af)[KS][FM], const V8 (&bf)[KS][FN], int lo, int hi) {
+    mfma_range_with(af, bf, lo, hi, [&](int) {});
+  };
+  // A compute phase of the ping-pong schedules issues the slab's kNMfma
+  // MFMAs from registers between two barriers.  (Issuing its last 2-8 after
+  // the closing barrier, so that they would cover the barrier's hand-over,
+  // measured 1-12 % slower on every large shape.)
+  constexpr int kNMfma = KS * FM * FN;
 
   auto compute = [&](const uint8_t* sA) {
 #pragma unroll
@@ -779,8 +827,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         wait_vmcnt<A2_CH + 2 * G::B_CH>();
         }
         phase_barrier();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mfma_step(af[ks], bf[ks], [&](int) {});
+        mfma_range(af, bf, 0, kNMfma);
         phase_barrier();
       });
       a_cur = (a_cur + 1 == NA) ? 0 : a_cur + 1;
@@ -835,12 +882,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       // loads just issued may stay in flight
       wait_vmcnt<(NS - 3) * G::LPS + A_CH>();
       phase_barrier();
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        mfma_step(af[ks], bf[ks], [&](int q) {
-          const int d = ks * FM * FN + q;
-          if (d < B_CH) issue_one(kt + NS - 1, smem + nxt * G::STAGE, A_CH + d);
-        });
+      static_assert(kNMfma >= B_CH, "the B loads go between the first MFMAs");
+      mfma_range_with(af, bf, 0, kNMfma, [&](int q) {
+        if (q < B_CH) issue_one(kt + NS - 1, smem + nxt * G::STAGE, A_CH + q);
+      });
       phase_barrier();
       cur = (cur + 1 == NS) ? 0 : cur + 1;
       nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
@@ -866,6 +911,14 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     nxt = (nxt + 1 == NS) ? 0 : nxt + 1;
   }
   }  // schedules 0 and 1
+
+  if constexpr (GEMMEPI_LDS_POISON != 0) {
+    // every load has landed (the drain above): poison the whole ring before
+    // the epilogue (and the split-K arrival flag) reuse it
+    for (int i = tid; i < SMEM_BYTES / 16; i += NT)
+      *(u32x4*)(smem + 16 * i) = u32x4{~0u, ~0u, ~0u, ~0u};
+    __syncthreads();
+  }
 
   // ---- split-K: partial tiles through the workspace ---------------------------
   // Each split writes its fp32 accumulators to its slot, element-major
@@ -1263,16 +1316,16 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   }
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT, int SCHED>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int NS, bool BT, int SCHED, int MT>
 hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
   static_assert(SCHED >= 0 && SCHED <= 2, "schedule");
   static_assert(SCHED == 0 || WM * WN == 8, "ping-pong pairs waves w and w + 4 on each SIMD");
   static_assert(SCHED != 1 || NS >= 3, "ping-pong issues each slab NS - 1 ahead from a compute phase");
-  static_assert(SCHED != 1 || (BK / kKStep) * (BM / WM / kMfma) * (BN / WN / kMfma) >=
-                                  GemmTile<BM, BN, BK, WM, WN, NS>::B_CH,
+  static_assert(SCHED != 1 || (BK / MfmaShape<MT>::kKStep) * (BM / WM / MT) * (BN / WN / MT) >=
+                                  GemmTile<BM, BN, BK, WM, WN, NS, MT>::B_CH,
                 "ping-pong issues one B load after each of the first MFMAs of a compute phase");
   const int blocks = a.tiles_m * a.tiles_n * (a.splits > 1 ? a.splits : 1);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, NS, BT, SCHED>), dim3(blocks), dim3(WM * WN * 64),
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, NS, BT, SCHED, MT>), dim3(blocks), dim3(WM * WN * 64),
                      0, s, a);
   return hipGetLastError();
 }
@@ -1280,9 +1333,9 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
 template <typename T, bool BT>
 hipError_t launch_by_tile(int tile, const GemmArgs& a, hipStream_t s) {
   switch (tile) {
-#define GEMMEPI_CASE(id, bm, bn, bk, wm, wn, ns, pp) \
-  case id:                                           \
-    return launch_tile<T, bm, bn, bk, wm, wn, ns, BT, pp>(a, s);
+#define GEMMEPI_CASE(id, bm, bn, bk, wm, wn, ns, pp, mt) \
+  case id:                                               \
+    return launch_tile<T, bm, bn, bk, wm, wn, ns, BT, pp, mt>(a, s);
     GEMMEPI_TILES(GEMMEPI_CASE)
 #undef GEMMEPI_CASE
     default:

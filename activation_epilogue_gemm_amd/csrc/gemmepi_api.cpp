@@ -27,8 +27,9 @@
 
 namespace gemmepi {
 
-#define GEMMEPI_TILE_ENTRY(id, bm, bn, bk, wm, wn, ns, sched) \
-  {bm, bn, bk, wm, wn, ns, sched, #bm "x" #bn "x" #bk "_w" #wm "x" #wn "_s" #ns "_p" #sched},
+#define GEMMEPI_TILE_ENTRY(id, bm, bn, bk, wm, wn, ns, sched, mt) \
+  {bm, bn, bk, wm, wn, ns, sched, mt,                              \
+   #bm "x" #bn "x" #bk "_w" #wm "x" #wn "_s" #ns "_p" #sched "_m" #mt},
 const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 #undef GEMMEPI_TILE_ENTRY
 
@@ -38,8 +39,9 @@ const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 // kNumCU * occ tiles; in one round a CU holds up to `occ` tiles that share
 // its MFMA units, so
 //   est = rounds * min(occ, ceil(tiles / kNumCU)) * BM * BN / eff.
-static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95, 1.08};
-static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 2, 3, 1, 1, 1};
+static const double kTileEff[kNumTiles] = {1.0, 0.95, 0.85, 0.70, 0.66, 0.56, 1.07, 0.95, 1.08,
+                                           0.60};
+static const int kTileOcc[kNumTiles] = {1, 1, 1, 1, 2, 3, 1, 1, 1, 1};
 // With B stored [N,K] both operands are K-contiguous; a 32-wide k slab then
 // fetches 64-byte row segments of both, which measured 0.83x on the
 // 65536 x 8192 x 16384 shape.  64-wide slabs fetch whole 128-byte lines and
@@ -76,6 +78,7 @@ struct gemmepi_plan_s {
   int tiles_m, tiles_n, group_m, xcd_remap;
   int sb_m, sb_n, xcd_m, xcd_n;
   int tuned;  // tile taken from a measured autotune result
+  int stage_b;  // B stored [K,N] is first copied [N,K] into the workspace
   int splits, kt_split;  // split-K: K ranges per tile, k slabs per range
   int k_per_wave;
   int refs;
@@ -163,7 +166,8 @@ gemmepi_status_t fail(gemmepi_status_t s, const char* fmt, ...) {
 
 constexpr uint32_t kAllFlags = GEMMEPI_FLAG_B_TRANS | GEMMEPI_FLAG_BIAS_PER_COL |
                                GEMMEPI_FLAG_UNFUSED | GEMMEPI_FLAG_VALIDATE |
-                               GEMMEPI_FLAG_NO_DECODE | GEMMEPI_FLAG_SPLIT_K;
+                               GEMMEPI_FLAG_NO_DECODE | GEMMEPI_FLAG_SPLIT_K |
+                               GEMMEPI_FLAG_STAGE_B;
 constexpr int kMaxSplits = 64;
 // Split-K cost model, fitted to a measured (tile, splits) sweep on one
 // MI355X: a split unit pays for its partial-tile round trip about as much
@@ -172,6 +176,11 @@ constexpr int kMaxSplits = 64;
 constexpr double kSplitCost = 200.0;
 constexpr double kSplitGain = 0.95;
 constexpr int64_t kMaxDim = 0x7FFFFFFF;
+// With GEMMEPI_FLAG_STAGE_B, B stored [K,N] is copied to [N,K] when the GEMM
+// has at least this many rows: the copy (read and write of N K elements)
+// then costs a few per cent of the GEMM, whose K-contiguous form ran ~10 %
+// faster than the [K,N] form on the 65536 x 8192 x 16384 shape.
+constexpr int64_t kStageMinM = 8192;
 
 bool log_enabled() {
   static int v = [] {
@@ -263,11 +272,13 @@ void describe(gemmepi_plan_s* p) {
                                "BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM",
                                "GELU_AUX_BIAS", "DGELU_BGRAD"};
   if (p->path == PATH_DECODE) {
+    const int rows = gemv_rows((int)p->M) > 0 ? gemv_rows((int)p->M) : 16;
     snprintf(buf, sizeof(buf),
-             "path=decode M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x grid=%lld waves=8 "
-             "k_per_wave=%d%s",
+             "path=decode M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x kernel=%s rows=%d "
+             "grid=%lld waves=8%s",
              (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
-             epis[p->epi], p->flags, (long long)((p->N + 15) / 16), p->k_per_wave,
+             epis[p->epi], p->flags, gemv_rows((int)p->M) > 0 ? "rowstream" : "mfma", rows,
+             (long long)((p->N + rows - 1) / rows),
              (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
   } else {
     const TileCfg& c = kTiles[p->tile];
@@ -276,11 +287,11 @@ void describe(gemmepi_plan_s* p) {
       snprintf(split_buf, sizeof(split_buf), " splits=%d kt_split=%d", p->splits, p->kt_split);
     snprintf(buf, sizeof(buf),
              "path=gemm M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x tile=%s tiles=%dx%d "
-             "raster=%s%s%s%s",
+             "raster=%s%s%s%s%s",
              (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
              epis[p->epi], p->flags, c.name, p->tiles_m, p->tiles_n,
              p->sb_m ? "chip16x16/xcd4x8" : (p->xcd_remap ? "xcd_remap,group8" : "group8"),
-             split_buf, p->tuned ? " tuned" : "",
+             split_buf, p->stage_b ? " stage_b" : "", p->tuned ? " tuned" : "",
              (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
   }
   p->info = buf;
@@ -338,7 +349,7 @@ GemmArgs gemm_args(const gemmepi_plan_s& p, const void* A, const void* B, void* 
   g.N = N;
   g.K = K;
   g.lda = K;
-  g.ldb = (p.flags & GEMMEPI_FLAG_B_TRANS) ? K : N;
+  g.ldb = ((p.flags & GEMMEPI_FLAG_B_TRANS) || p.stage_b) ? K : N;
   g.ldo = N;
   g.aux_words = (N + 31) / 32;
   g.tiles_m = p.tiles_m;
@@ -368,10 +379,18 @@ void set_split(gemmepi_plan_s* p, int splits) {
 size_t counter_bytes(const gemmepi_plan_s& p) {
   return ((size_t)p.tiles_m * p.tiles_n * 4 + 255) / 256 * 256;
 }
+// Staged plans keep the [N,K] copy of B at the start of the workspace.
+size_t stage_bytes(const gemmepi_plan_s& p) {
+  return p.stage_b ? ((size_t)p.N * (size_t)p.K * 2 + 255) / 256 * 256 : 0;
+}
 size_t workspace_bytes(const gemmepi_plan_s& p) {
-  if (p.path != PATH_GEMM || p.splits <= 1) return 0;
-  const TileCfg& c = kTiles[p.tile];
-  return counter_bytes(p) + (size_t)p.tiles_m * p.tiles_n * p.splits * c.bm * c.bn * 4;
+  if (p.path != PATH_GEMM) return 0;
+  size_t b = stage_bytes(p);
+  if (p.splits > 1) {
+    const TileCfg& c = kTiles[p.tile];
+    b += counter_bytes(p) + (size_t)p.tiles_m * p.tiles_n * p.splits * c.bm * c.bn * 4;
+  }
+  return b;
 }
 
 // Tile, grid shape and raster of a tiled-GEMM plan.
@@ -475,10 +494,22 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
         if (splits == 0) splits = 1;
       }
     }
-    if (splits == 0)
-      choose_split(M, N, K, bt, &tile, &splits);  // keeps an explicit tile
-    else if (tile < 0)
-      tile = choose_tile(M, N, K, bt);
+    // B as the kernel reads it: staged plans read the [N,K] copy
+    bool stage = (flags & GEMMEPI_FLAG_STAGE_B) && !bt && !norm_epi && M >= kStageMinM;
+    const int tile0 = tile, splits0 = splits;
+    for (;;) {
+      const bool bt_k = bt || stage;
+      if (splits == 0)
+        choose_split(M, N, K, bt_k, &tile, &splits);  // keeps an explicit tile
+      else if (tile < 0)
+        tile = choose_tile(M, N, K, bt_k);
+      if (!stage || splits <= 1) break;
+      // a shape that wants K split is too small to repay the copy
+      stage = false;
+      tile = tile0;
+      splits = splits0;
+    }
+    p->stage_b = stage ? 1 : 0;
     set_tile(p, tile);
     set_split(p, splits);
     if ((int64_t)p->tiles_m * p->tiles_n * p->splits > 0x7FFFFFFFLL) {
@@ -507,7 +538,7 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
                               void* aux, void* out, void* ws, size_t ws_bytes, void* stream,
                               bool ws_static = false) {
   const int epi = p.epi;
-  const bool bt = p.flags & GEMMEPI_FLAG_B_TRANS;
+  const bool bt = (p.flags & GEMMEPI_FLAG_B_TRANS) || p.stage_b;  // as the kernel reads B
   const bool per_col = p.flags & GEMMEPI_FLAG_BIAS_PER_COL;
   const bool unfused = p.flags & GEMMEPI_FLAG_UNFUSED;
   const bool bgrad_epi = epi == EPI_DRELU_BGRAD || epi == EPI_DGELU_BGRAD;
@@ -532,8 +563,8 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
   if (ws_need > 0) {
     if (!ws)
       return fail(GEMMEPI_ERR_INVALID_VALUE,
-                  "execute: the plan splits K and needs a workspace of %zu bytes "
-                  "(gemmepi_execute_ws)", ws_need);
+                  "execute: the plan %s and needs a workspace of %zu bytes "
+                  "(gemmepi_execute_ws)", p.stage_b ? "stages B" : "splits K", ws_need);
     if (ws_bytes < ws_need)
       return fail(GEMMEPI_ERR_INVALID_VALUE, "execute: workspace of %zu bytes, the plan needs %zu",
                   ws_bytes, ws_need);
@@ -560,10 +591,11 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
   hipError_t e = hipSuccess;
   (void)hipGetLastError();  // clear a stale error so it is not blamed on this call
 
-  if (ws_need > 0 && ws_static) {
+  if (p.splits > 1 && ws_static) {
     // a fill kernel rather than hipMemsetAsync, so a captured stream
     // replays it correctly
-    e = launch_fill_f32((float*)ws, (int64_t)(counter_bytes(p) / 4), 0.0f, s);
+    e = launch_fill_f32((float*)((uint8_t*)ws + stage_bytes(p)), (int64_t)(counter_bytes(p) / 4),
+                        0.0f, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "scratch counter fill: %s", hipGetErrorString(e));
   }
   if (bgrad_epi) {
@@ -596,9 +628,16 @@ gemmepi_status_t execute_impl(const gemmepi_plan_s& p, const void* A, const void
     g.aux_ld = aux_ld;
     g.epi = core_epi;
     g.bias_per_col = per_col ? 1 : 0;
-    if (ws_need > 0) {
-      g.counters = (uint32_t*)ws;
-      g.ws = (float*)((uint8_t*)ws + counter_bytes(p));
+    if (p.stage_b) {
+      // B [K,N] -> its [N,K] copy at the start of the workspace
+      e = launch_transpose16(B, ws, K, N, s);
+      if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "B staging copy: %s", hipGetErrorString(e));
+      g.B = ws;
+    }
+    if (p.splits > 1) {
+      uint8_t* w = (uint8_t*)ws + stage_bytes(p);
+      g.counters = (uint32_t*)w;
+      g.ws = (float*)(w + counter_bytes(p));
     }
     e = launch_gemm(p.dtype, bt, p.tile, g, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
@@ -670,7 +709,7 @@ gemmepi_status_t gemmepi_execute_noalloc(gemmepi_plan_t plan, const void* A, con
   if (need == 0) return execute_impl(*plan, A, B, bias, aux, out, nullptr, 0, stream);
   if (need > kScratchBytes)
     return fail(GEMMEPI_ERR_UNSUPPORTED,
-                "execute_noalloc: the plan's split-K workspace is %zu bytes, more than the "
+                "execute_noalloc: the plan's workspace is %zu bytes, more than the "
                 "library's static scratch of %zu bytes (use gemmepi_execute_ws)",
                 need, kScratchBytes);
   gemmepi_status_t st = check_device();
@@ -826,8 +865,8 @@ gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void
     return fail(GEMMEPI_ERR_UNSUPPORTED, "autotune: norm plans are not tuned");
   if (p.tile_req >= 0)
     return fail(GEMMEPI_ERR_INVALID_VALUE, "autotune: the plan has an explicit tile");
-  if (p.splits > 1)
-    return fail(GEMMEPI_ERR_UNSUPPORTED, "autotune: split-K plans are not tuned");
+  if (p.splits > 1 || p.stage_b)
+    return fail(GEMMEPI_ERR_UNSUPPORTED, "autotune: split-K and B-staging plans are not tuned");
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {

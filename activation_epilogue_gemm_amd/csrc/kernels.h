@@ -77,19 +77,25 @@ struct DecodeArgs {
 // One tile configuration of the tiled GEMM.
 struct TileCfg {
   int bm, bn, bk, wm, wn, ns, sched;
+  int mfma;  // 16: v_mfma_f32_16x16x32, 32: v_mfma_f32_32x32x16
   const char* name;
 };
 
-constexpr int kNumTiles = 9;
+constexpr int kNumTiles = 10;
 extern const TileCfg kTiles[kNumTiles];
 
 // Launchers (defined in the per-dtype/per-layout instantiation files).
 // Return hipSuccess or the launch error.
 hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
+// Rows of W per workgroup of the row-streaming decode kernel for M tokens,
+// or 0 when the MFMA decode kernel (16 rows per workgroup) runs.
+int gemv_rows(int M);
 
 // Unfused baseline kernels and helpers (elementwise.hip).
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// dst [N, K] = src [K, N] transposed, 16-bit elements; K and N multiples of 8
+hipError_t launch_transpose16(const void* src, void* dst, int K, int N, hipStream_t s);
 hipError_t launch_bias_add(int dtype, void* out, const void* bias, int M, int N, int ldo,
                            int per_col, hipStream_t s);
 hipError_t launch_activation(int dtype, int epi, void* out, uint32_t* aux, int M, int N, int ldo,

@@ -112,7 +112,17 @@ enum {
    * plan needs a device workspace (gemmepi_workspace_bytes) and runs
    * through gemmepi_execute_ws.  No effect on the decode kernel and the
    * norm epilogues. */
-  GEMMEPI_FLAG_SPLIT_K = 1u << 5
+  GEMMEPI_FLAG_SPLIT_K = 1u << 5,
+  /* Let plan() stage B stored [K,N] (no B_TRANS): each execution first
+   * copies B into a K-contiguous [N,K] copy in the workspace, then runs the
+   * GEMM on it.  The copy reads and writes N K elements once; plan() takes
+   * it only for GEMMs of at least 8192 rows that do not split K, where the
+   * GEMM on K-contiguous B (slabs read with 128-bit LDS reads rather than
+   * transposing ones) gains more than the copy costs.  Such a plan needs a
+   * device workspace (gemmepi_workspace_bytes) and runs through
+   * gemmepi_execute_ws.  No effect with B_TRANS, on the decode kernel and on
+   * the norm epilogues. */
+  GEMMEPI_FLAG_STAGE_B = 1u << 6
 };
 
 /* Opaque, reference-counted handle to a cached plan. */
@@ -173,8 +183,9 @@ gemmepi_status_t gemmepi_plan_split(gemmepi_plan_t* plan, int64_t M, int64_t N, 
                                     uint32_t flags, int32_t tile_id, int32_t splits);
 
 /*
- * Device workspace a plan needs, in bytes: 0 unless the plan splits K.
- * Then it is 4 bytes per output tile (arrival counters, padded to 256
+ * Device workspace a plan needs, in bytes: 0 unless the plan stages B or
+ * splits K.  A staged plan needs 2 N K bytes (padded to 256) for the copy of
+ * B; a split plan 4 bytes per output tile (arrival counters, padded to 256
  * bytes) plus one fp32 partial tile per (tile, split).  NULL plan: 0.
  */
 size_t gemmepi_workspace_bytes(gemmepi_plan_t plan);
@@ -213,14 +224,15 @@ gemmepi_status_t gemmepi_execute(gemmepi_plan_t plan, const void* A, const void*
                                  void* aux, void* out, void* stream);
 /* (A plan with a norm epilogue is rejected by gemmepi_execute with
  * INVALID_VALUE; it runs through gemmepi_execute_norm below.  A plan that
- * splits K is rejected too: it runs through gemmepi_execute_ws.) */
+ * splits K or stages B is rejected too: it runs through gemmepi_execute_ws.) */
 
 /*
  * gemmepi_execute with a caller-owned device workspace, which a plan that
- * splits K needs (gemmepi_workspace_bytes > 0); the vendor library's matmul
+ * splits K or stages B needs (gemmepi_workspace_bytes > 0); the vendor library's matmul
  * likewise takes its workspace from the caller ("Bias fusion with cuBLASLt
  * in PyTorch inference", body).  For a plan that does not split K it is
- * identical to gemmepi_execute and the workspace is ignored.
+ * identical to gemmepi_execute and the workspace is ignored.  A staged plan
+ * overwrites the workspace's copy of B on every execution.
  *
  *   workspace        device memory, 256-byte aligned, at least
  *                    gemmepi_workspace_bytes(plan) bytes.  Its counter
@@ -259,8 +271,9 @@ gemmepi_status_t gemmepi_execute_ws(gemmepi_plan_t plan, const void* A, const vo
  * through gemmepi_execute_ws.
  *
  * Arguments as gemmepi_execute.  Errors: as gemmepi_execute, plus
- * UNSUPPORTED when the plan's workspace (gemmepi_workspace_bytes) exceeds
- * the static array, HIP when its device address cannot be looked up.
+ * UNSUPPORTED when the plan's workspace (gemmepi_workspace_bytes: split-K
+ * partials, or a staged copy of B) exceeds the static array, HIP when its
+ * device address cannot be looked up.
  */
 gemmepi_status_t gemmepi_execute_noalloc(gemmepi_plan_t plan, const void* A, const void* B,
                                          void* bias, void* aux, void* out, void* stream);
@@ -286,7 +299,7 @@ size_t gemmepi_noalloc_scratch_bytes(void);
  *            milliseconds per execution
  * Not thread-safe against executions of the same plan on other threads.
  * Errors: INVALID_VALUE (null plan, reps, a plan made with an explicit
- * tile), UNSUPPORTED (decode, norm or split-K plans), the errors of
+ * tile), UNSUPPORTED (decode, norm, split-K or B-staging plans), the errors of
  * gemmepi_execute, HIP (timing, or the cache file could not be written).
  */
 gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void* B, void* bias,

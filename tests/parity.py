@@ -11,9 +11,11 @@ oracle's z.  For DGELU_BGRAD the accumulator's error reaches dZ = acc gelu'(z)
 scaled by |gelu'(z)| <= 1.129 (its maximum, at z = sqrt 2), so the absolute
 term of dZ and of bgrad is multiplied by that bound.  The unfused sequence
 sums dZ values that were rounded to the dtype (once for DRELU, twice for
-DGELU: the GEMM's output and the product with gelu'), so its bgrad also gets
-2 u sum_m |dZ[m, n]|, the standard bound for a sum of terms each within a
-relative 2 u of the exact one (u the dtype's unit roundoff).
+DGELU: the GEMM's output and the product with gelu').  In fp16 its bgrad is
+held to the same formula; in bf16, whose unit roundoff u = 2^-8 is 8 times
+fp16's, the formula also gets 2 u sum_m |dZ[m, n]|, the worst-case bound of
+that rounding.  The test log reports each bgrad's error against the
+tolerance used and, unfused, against that rounding bound.
 """
 from __future__ import annotations
 
@@ -21,6 +23,23 @@ import numpy as np
 
 import activation_epilogue_gemm_amd as ge
 from oracle import oracle as O
+
+
+def tile_table():
+    """The tiled GEMM's tile configurations, read from the table the kernels
+    and the planner are built from (csrc/gemm_tiles.h): one dict per tile."""
+    import os
+    import re
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "activation_epilogue_gemm_amd", "csrc", "gemm_tiles.h")
+    keys = ("id", "bm", "bn", "bk", "wm", "wn", "ns", "sched", "mfma")
+    rows = [dict(zip(keys, map(int, m.groups())))
+            for m in re.finditer(r"X\(" + r",\s*".join([r"(\d+)"] * 9) + r"\)", open(path).read())]
+    assert [r["id"] for r in rows] == list(range(len(rows))), "tile ids must be 0..n-1"
+    return rows
+
+
+NUM_TILES = len(tile_table())
 
 
 def torch_dtype(dtype: str):
@@ -237,16 +256,31 @@ def check_zaux(case, got_bits: np.ndarray, ref, A_bits=None, label: str = ""):
 
 
 def check_bgrad(case, got: np.ndarray, ref, label: str = "", unfused: bool = False):
+    """bgrad against the oracle's, to the parity formula.  The unfused path
+    sums dZ values already rounded to the dtype; in fp16 (u = 2^-11) the
+    formula covers that rounding as it stands, in bf16 (u = 2^-8) it does not
+    (a 333-row DGELU case measured 1.77 times the formula), so bf16 adds the
+    worst-case bound of that rounding, 2 u sum_m |dZ[m, n]|.  Returns (and
+    logs) the largest err / tol, and for the unfused path the largest err
+    over that rounding bound."""
+    import sys
     tol = 1e-2 * np.abs(ref.bgrad.astype(np.float64)) + grad_scale(case) * abs_term(case)
-    if unfused:
-        tol = tol + 2.0 * UNIT_ROUNDOFF[case.dtype] * ref.bgrad_abs
     err = np.abs(got.astype(np.float64) - ref.bgrad.astype(np.float64))
+    extra = ""
+    if unfused:
+        worst = 2.0 * UNIT_ROUNDOFF[case.dtype] * ref.bgrad_abs
+        extra = f"; err / (2u sum|dZ|) max {float((err / np.maximum(worst, 1e-300)).max()):.3g}"
+        if case.dtype == "bf16":
+            tol = tol + worst
+    ratio = float((err / tol).max())
+    print(f"[bgrad] {label} {case.name}: max err/tol {ratio:.3g}{extra}", file=sys.stderr,
+          flush=True)
     bad = err > tol
     if bad.any():
         i = np.argwhere(bad)[:5].ravel()
         raise AssertionError(f"{label} {case.name}: bgrad {int(bad.sum())} out of tolerance; "
                              f"{[(int(j), float(got[j]), float(ref.bgrad[j])) for j in i]}")
-    return float((err / tol).max())
+    return ratio
 
 
 # ---------------------------------------------------------------- GEMM + residual + norm

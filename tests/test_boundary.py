@@ -299,7 +299,7 @@ def test_planner_prefers_64_wide_slabs_when_b_is_transposed():
     with ge.plan(65536, 8192, 16384, "f16", "RELU_AUX_BIAS", ge.FLAG_B_TRANS) as p:
         assert f"tile={ge.tile_name(8)}" in p.info(), p.info()   # A in 64-wide slabs
     # without schedule 2 (explicit tiles only), B [N,K] prefers 64-wide slabs
-    assert ge.tile_name(8).endswith("_p2")
+    assert "_p2_" in ge.tile_name(8)
 
 
 def test_split_flag_chooses_only_for_wave_quantised_shapes():

@@ -17,7 +17,7 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check_out, check_zaux
+from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check_out, check_zaux
 
 pytestmark = pytest.mark.gpu
 
@@ -76,7 +76,6 @@ def run_and_check(c, flags=0, tile=-1, exact=False, guard=0, label=""):
 
 
 # ---------------------------------------------------------------- every tile, exact
-NUM_TILES = 9
 
 
 def test_tile_count():
@@ -133,7 +132,7 @@ def test_unfused_matches_oracle(epi, dtype):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_decode_path(T, dtype):
     for epi in ("DEFAULT", "BIAS", "RELU_BIAS", "GELU_BIAS"):
-        for (N, K) in ((200, 520), (4096, 4096), (24, 8)):
+        for (N, K) in ((200, 520), (4096, 4096), (24, 8), (203, 4104)):
             c = wl.random_case(T, N, K, dtype, epi, True, True, 300 + T + N)
             r = GpuRun(c)
             assert "path=decode" in r.info, r.info
@@ -207,8 +206,9 @@ def test_config2_ffn_full(variant):
         rd.close()
 
 
-def _large(c, rows_count=4096):
-    """4096 seed-chosen rows (always 0 and M-1) of out / mask, all of bgrad."""
+def _large(c, rows_count=4096, flag_sets=(0, ge.FLAG_UNFUSED)):
+    """4096 seed-chosen rows (always 0 and M-1) of out / mask, all of bgrad,
+    for each of the plan flag sets (one oracle result serves them all)."""
     import torch
     cfg = 4 if c.epilogue in BGRAD_EPIS else 3
     rows = wl.sample_rows(c.M, rows_count, wl.row_sample_seed(cfg))
@@ -219,9 +219,11 @@ def _large(c, rows_count=4096):
     else:
         ref = O.gemm_epilogue(c.host_A(rows), B, c.bias[rows], None, len(rows), c.N, c.K,
                               c.dtype, c.epilogue, c.b_trans, c.bias_per_col)
-    for flags in (0, ge.FLAG_UNFUSED):
+    for flags in flag_sets:
         r = GpuRun(c, flags=flags)
         say("large", c.name, r.info)
+        if flags & ge.FLAG_STAGE_B:
+            assert "stage_b" in r.info, r.info
         r.run()
         check_out(c, r.out_bits(rows), ref, label=f"large-{flags}")
         if c.epilogue == "RELU_AUX_BIAS":
@@ -237,9 +239,14 @@ def _large(c, rows_count=4096):
         torch.cuda.empty_cache()
 
 
+# the benchmark runs the two large workloads with B staged ([K,N] copied to
+# [N,K] in the workspace, GEMMEPI_FLAG_STAGE_B): both forms, fused and unfused
+STAGED = (0, ge.FLAG_UNFUSED, ge.FLAG_STAGE_B, ge.FLAG_STAGE_B | ge.FLAG_UNFUSED)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_config3_relu_aux_full(dtype):
-    _large(wl.config3_relu_aux(dtype))
+    _large(wl.config3_relu_aux(dtype), flag_sets=STAGED)
 
 
 def test_config3_relu_aux_full_b_stored_nk():
@@ -253,7 +260,7 @@ def test_config3_relu_aux_full_b_stored_nk():
 
 
 def test_config4_drelu_bgrad_full():
-    _large(wl.config4_drelu_bgrad())
+    _large(wl.config4_drelu_bgrad(), flag_sets=STAGED)
 
 
 def test_dgelu_bgrad_full():

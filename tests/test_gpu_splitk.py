@@ -14,12 +14,11 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check_out, check_zaux
+from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check_out, check_zaux
 
 pytestmark = pytest.mark.gpu
 
 EPIS = list(O.EPILOGUES)
-NUM_TILES = 9
 
 
 def say(*a):

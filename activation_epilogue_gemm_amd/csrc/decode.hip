@@ -36,6 +36,12 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Cache policy of the weight loads (the aux operand of the buffer load):
+// 0 = normal, 2 = non-temporal (streamed, evict-first in L2).
+#ifndef GEMMEPI_DECODE_W_POLICY
+#define GEMMEPI_DECODE_W_POLICY 0
+#endif
+
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeUnroll = 16;            // 32-wide k steps per W batch
 constexpr int kDecodeWin = 32 * kDecodeUnroll;  // k window of one batch (512)
@@ -100,7 +106,8 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
 #pragma unroll
     for (int u = 0; u < kDecodeUnroll; ++u) {
       const int kk = k + u * 32 + kg * 8;
-      wv[u] = buffer_load16(rW, (kk < kend && w_ok) ? w_row + (uint32_t)kk * 2u : kOOB);
+      wv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          rW, (kk < kend && w_ok) ? w_row + (uint32_t)kk * 2u : kOOB, 0, GEMMEPI_DECODE_W_POLICY);
     }
 #pragma unroll
     for (int t = 0; t < TB; ++t) *(u32x4*)(xw + xwin_off(t, lane)) = xl[t];
@@ -138,6 +145,133 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
   }
 }
 
+// ---- row-streaming decode for one or two tokens --------------------------
+// With M <= 2 the products are too few to need the matrix cores, and the
+// weight stream is best read the way a plain streaming read is fastest: one
+// contiguous 1 KiB per load instruction, and many small workgroups (the
+// stream-read sweep of the benchmark peaks at 32 KiB per workgroup).  A
+// workgroup owns R consecutive rows of W (R = 4: 32 KiB of a 4096-wide
+// row block); wave w covers k in [512 w, 512 w + 512) + 4096 j, and lane l
+// of it the 8 consecutive k at 8 l, so load r of a lane reads row r's
+// 16 bytes there and the wave's 64 lanes read 1 KiB of one row.  Each lane
+// multiplies its W chunks with the same k chunk of every token on the VALU
+// (v_dot2: fp32 accumulation of exact fp16/bf16 products), the R x TB
+// partial sums are reduced over the wave's lanes by a butterfly, then over
+// the 8 waves through LDS, and wave 0 applies the epilogue.
+// (each vector element is copied to a scalar before the bit cast: this
+// compiler's __builtin_bit_cast of an ext_vector element expression reads
+// element 0 whatever the index)
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float c, _Float16) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wi = w[i], xi = x[i];
+    c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, wi), __builtin_bit_cast(f16x2, xi), c,
+                               false);
+  }
+  return c;
+}
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float c, __bf16) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wi = w[i], xi = x[i];
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wi), __builtin_bit_cast(bf16x2, xi),
+                                        c, false);
+  }
+  return c;
+}
+
+template <typename T, int R, int TB>
+__global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArgs p) {
+  __shared__ float red[kDecodeWaves][R * TB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n0 = blockIdx.x * R;
+  const int Mt = p.M;
+  const __amdgpu_buffer_rsrc_t rW = make_rsrc((const uint8_t*)p.W + (size_t)n0 * p.ldw * 2);
+  const __amdgpu_buffer_rsrc_t rX = make_rsrc(p.x);
+  float acc[R][TB];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[r][t] = 0.0f;
+  constexpr int kWin = kDecodeWaves * 512;  // k covered by one pass of the workgroup
+  for (int kw = 0; kw < p.K; kw += kWin) {
+    const int k = kw + wave * 512 + lane * 8;
+    const bool k_ok = k < p.K;
+    u32x4 wv[R], xv[TB];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      wv[r] = __builtin_amdgcn_raw_buffer_load_b128(
+          rW, (k_ok && n0 + r < p.N) ? (uint32_t)(r * p.ldw + k) * 2u : kOOB, 0,
+          GEMMEPI_DECODE_W_POLICY);
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+      xv[t] = buffer_load16(rX, (k_ok && t < Mt) ? (uint32_t)(t * p.ldx + k) * 2u : kOOB);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < TB; ++t) acc[r][t] = dot8(wv[r], xv[t], acc[r][t], T{});
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      float v = acc[r][t];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      acc[r][t] = v;
+    }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int t = 0; t < TB; ++t) red[wave][r * TB + t] = acc[r][t];
+  }
+  __syncthreads();
+  if (wave != 0 || lane >= R * TB) return;
+  const int r = lane / TB, t = lane - (lane / TB) * TB;
+  const int n = n0 + r;
+  if (n >= p.N || t >= Mt) return;
+  float z = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDecodeWaves; ++w) z += red[w][lane];
+  if (p.epi != EPI_DEFAULT) {
+    const T* bias = (const T*)p.bias;
+    z += to_f32(bias[p.bias_per_col ? n : t]);
+  }
+  float y = z;
+  if (p.epi == EPI_GELU_BIAS) y = gelu_erf(z);
+  else if (p.epi == EPI_RELU_BIAS) y = z > 0.0f ? z : 0.0f;
+  ((T*)p.out)[(size_t)t * p.ldo + n] = from_f32<T>(y);
+}
+
+// Rows per workgroup of the row-streaming kernel for M tokens; 0: the MFMA
+// decode kernel above.  Measured over the 16 rotated 4096 x 4096 weights
+// against the MFMA kernel: 4 rows 7.96 against 8.44 us at M = 1, 8.43
+// against 8.78 at M = 2, but 12.6 against 8.8 at M = 4 (each workgroup
+// re-reads every token row, 32 MiB in all, and the VALU products grow
+// with M); 8 rows per workgroup were slower at every M.
+#ifndef GEMMEPI_GEMV_ROWS
+#define GEMMEPI_GEMV_ROWS 4
+#endif
+int gemv_rows(int M) { return M <= 2 ? GEMMEPI_GEMV_ROWS : 0; }
+
+template <typename T>
+static void launch_gemv_t(const DecodeArgs& a, int R, hipStream_t s) {
+  const dim3 block(kDecodeWaves * 64);
+  const dim3 grid((a.N + R - 1) / R);
+#define GEMMEPI_GEMV(RR, TT) hipLaunchKernelGGL((gemv_kernel<T, RR, TT>), grid, block, 0, s, a)
+  if (R == 8) {
+    if (a.M <= 1) GEMMEPI_GEMV(8, 1);
+    else GEMMEPI_GEMV(8, 2);
+  } else {
+    if (a.M <= 1) GEMMEPI_GEMV(4, 1);
+    else GEMMEPI_GEMV(4, 2);
+  }
+#undef GEMMEPI_GEMV
+}
+
 template <typename T>
 static void launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((a.N + 15) / 16), block(kDecodeWaves * 64);
@@ -155,10 +289,17 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) {
   if (a.M < 1 || a.M > 16) return hipErrorInvalidValue;
-  if (dtype == DT_F16)
+  const int R = gemv_rows(a.M);
+  if (R > 0 && a.K % 8 == 0) {
+    if (dtype == DT_F16)
+      launch_gemv_t<_Float16>(a, R, s);
+    else
+      launch_gemv_t<__bf16>(a, R, s);
+  } else if (dtype == DT_F16) {
     launch_decode_t<_Float16>(a, s);
-  else
+  } else {
     launch_decode_t<__bf16>(a, s);
+  }
   return hipGetLastError();
 }
 

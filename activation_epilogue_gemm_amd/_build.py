@@ -22,6 +22,10 @@ LIB = os.path.join(PKG, "libgemmepi.so")
 # measurement helpers used by the benchmark only, in a library of their own
 MEASURE_SOURCES = ["measure.hip"]
 MEASURE_LIB = os.path.join(PKG, "libgemmepi_measure.so")
+# the LDS race-detector build of the same library (GEMMEPI_LDS_POISON=1), for
+# tests/test_gpu_lds_poison.py only
+POISON_LIB = os.path.join(PKG, "libgemmepi_poison.so")
+POISON_FLAGS = ["-DGEMMEPI_LDS_POISON=1"]
 
 SOURCES = [
     "gemmepi_api.cpp",
@@ -58,8 +62,8 @@ def common_flags(extra=()):
     ]
 
 
-def _compile(src: str, extra=()) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra=(), objdir: str = "") -> str:
+    obj = os.path.join(objdir or BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc(), *common_flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -69,29 +73,37 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = True, jobs: int = 0, extra=()) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    t0 = time.time()
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    mobjs = [_compile(src, extra) for src in MEASURE_SOURCES]
-    tmp = MEASURE_LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *mobjs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, MEASURE_LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True, jobs: int = 0, extra=(), poison: bool = True) -> str:
+    """Compile every source and link the shared library (plus the measurement
+    library and, with ``poison``, the LDS race-detector build); returns the
+    library's path."""
+    pdir = os.path.join(BUILD, "poison")
+    os.makedirs(pdir, exist_ok=True)
+    t0 = time.time()
+    jobs = jobs or max(1, (os.cpu_count() or 4))
+    units = [(s, tuple(extra), "") for s in SOURCES + MEASURE_SOURCES]
+    if poison:
+        units += [(s, tuple(extra) + tuple(POISON_FLAGS), pdir) for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda u: _compile(*u), units))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + len(MEASURE_SOURCES)], MEASURE_LIB)
+    if poison:
+        _link(objs[n + len(MEASURE_SOURCES):], POISON_LIB)
     if verbose:
-        print(f"[gemmepi] built {LIB} and {MEASURE_LIB} in {time.time() - t0:.1f}s",
-              file=sys.stderr)
+        print(f"[gemmepi] built {LIB}, {os.path.basename(MEASURE_LIB)}"
+              f"{' and ' + os.path.basename(POISON_LIB) if poison else ''} "
+              f"in {time.time() - t0:.1f}s", file=sys.stderr)
     return LIB
 
 

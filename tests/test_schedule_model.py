@@ -14,19 +14,52 @@ happened in a phase before p.
 
 The issue order and wait counts below are the kernel's (A in pairs of
 slabs in a ring of 3; B in single slabs in a ring of 4, or, stored [N,K], in
-pairs in a ring of 2), written out for tile 8 (A2 = 4 loads per A pair,
-B = 2 per B slab, B2 = 4 per B pair).  A negative control loosens one wait
-count and must be caught.
+pairs in a ring of 2).  The loads per wave of an A pair (A2), a B slab (B1)
+and a B pair (B2) follow from each schedule-2 tile's row of the tile table
+(csrc/gemm_tiles.h), and the wait counts are checked against the kernel
+source's: the vmcnt expressions of its schedule-2 section must be the ones
+this model evaluates.  A negative control loosens one wait count and must be
+caught.
 """
+import os
+import re
+
 import pytest
 
-A2, B1, B2 = 4, 2, 4
+from parity import tile_table
+
+KERNEL = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "activation_epilogue_gemm_amd", "csrc", "gemm_mfma.hpp")
+# the schedule-2 waits of the kernel, in source order: B stored [N,K]
+# prologue, B [K,N] prologue, first and second load phase of a pair with B
+# pairs, the load phase with single B slabs, the drain after the loop
+KERNEL_WAITS = ["A2_CH", "G::B_CH + A2_CH + G::B_CH", "A2_CH + B2_CH", "A2_CH",
+                "A2_CH + 2 * G::B_CH", "0"]
+SCHED2 = [t for t in tile_table() if t["sched"] == 2]
 
 
-def schedule(bpair: bool, npairs: int, loose: bool = False):
+def load_counts(t):
+    """(A2, B1, B2): 16-byte loads per lane of one wave for an A pair, a B
+    slab and a B pair of the tile (every 64-lane load fills 1 KiB)."""
+    nt = t["wm"] * t["wn"] * 64
+    per = nt * 16
+    return (t["bm"] * 2 * t["bk"] * 2 // per, t["bn"] * t["bk"] * 2 // per,
+            t["bn"] * 2 * t["bk"] * 2 // per)
+
+
+def test_model_waits_are_the_kernels():
+    src = open(KERNEL).read()
+    a = src.index("if constexpr (SCHED == 2) {")
+    b = src.index("// prologue: the first NS-1 slabs", a)
+    waits = [re.sub(r"\s+", " ", w).strip() for w in re.findall(r"wait_vmcnt<(.*?)>\(\)", src[a:b])]
+    assert waits == KERNEL_WAITS, waits
+
+
+def schedule(bpair: bool, npairs: int, loose: bool = False, counts=(4, 2, 4)):
     """Per-wave program: list of (kind, payload) in program order, with the
     barrier phase of each step relative to the wave's group (load phase of
     slab i is local phase 2i; the prologue is phase -1)."""
+    A2, B1, B2 = counts
     prog = []
     if bpair:
         prog += [("issue", ("A", 0, 0, A2)), ("issue", ("BP", 0, 0, B2)),
@@ -85,8 +118,8 @@ def run_group(prog, g):
     return retired_at, reads, issues
 
 
-def check(bpair: bool, npairs: int = 12, loose: bool = False):
-    prog = schedule(bpair, npairs, loose)
+def check(bpair: bool, npairs: int = 12, loose: bool = False, counts=(4, 2, 4)):
+    prog = schedule(bpair, npairs, loose, counts)
     groups = [run_group(prog, g) for g in (0, 1)]
     last_slab = 2 * npairs - 1
     # readiness: every read in phase p needs both groups' shares retired before p
@@ -117,12 +150,19 @@ def check(bpair: bool, npairs: int = 12, loose: bool = False):
     return last_slab
 
 
+@pytest.mark.parametrize("tile", SCHED2, ids=[f"tile{t['id']}" for t in SCHED2])
 @pytest.mark.parametrize("bpair", [False, True])
-def test_schedule2_waits_and_stage_reuse(bpair):
-    check(bpair)
+def test_schedule2_waits_and_stage_reuse(bpair, tile):
+    check(bpair, counts=load_counts(tile))
 
 
+@pytest.mark.parametrize("tile", SCHED2, ids=[f"tile{t['id']}" for t in SCHED2])
 @pytest.mark.parametrize("bpair", [False, True])
-def test_schedule2_model_catches_a_loose_wait(bpair):
+def test_schedule2_model_catches_a_loose_wait(bpair, tile):
     with pytest.raises(AssertionError):
-        check(bpair, loose=True)
+        check(bpair, loose=True, counts=load_counts(tile))
+
+
+def test_schedule2_tile_exists():
+    assert SCHED2, "no schedule-2 tile in the tile table"
+    assert load_counts(SCHED2[0]) == (4, 2, 4)

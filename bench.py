@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = 2516.6     # MI355X dense fp16/bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
 PEAK_GBS = 8000.0        # MI355X HBM3E
 DECODE_COPIES = 16
+FFN_COPIES = 3           # 3 x (W1 + W2) = 516 MiB, beyond the 256 MB Infinity Cache
 
 
 def log(*a):
@@ -62,6 +63,10 @@ def parse():
     ap.add_argument("--profile-layouts", action="store_true",
                     help="only run the C3 fp16 fused kernel twice with B stored [K,N] (as the "
                          "workload) and twice with the same B stored [N,K], for rocprofv3 --pmc runs")
+    ap.add_argument("--profile-workloads", action="store_true",
+                    help="only run the 1 GiB copy (calibration) and two fused executions of each "
+                         "selected workload (--only, default c0,c2,c4), one after another, for "
+                         "rocprofv3 --pmc runs of the tiles other than C3's")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only run the 1 GiB copy (calibration) and 16 decode calls each at "
                          "T = 1 and T = 16 over 16 rotated weight copies, for rocprofv3 --pmc runs")
@@ -169,7 +174,9 @@ class Workload:
         # FLAG_SPLIT_K: plan() may split K for the wave-quantised shapes (C0,
         # the 512-token down-projection); its workspace is allocated by the
         # plan at the first (warm-up) execution
-        f = flags | ge.FLAG_SPLIT_K | (ge.FLAG_B_TRANS if c.b_trans else 0) | \
+        # FLAG_STAGE_B: plan() may copy a [K,N] B to [N,K] in the workspace
+        # first (it does for the two large workloads, C3 and C4)
+        f = flags | ge.FLAG_SPLIT_K | ge.FLAG_STAGE_B | (ge.FLAG_B_TRANS if c.b_trans else 0) | \
             (ge.FLAG_BIAS_PER_COL if c.bias_per_col else 0)
         self.fused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f)
         self.unfused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, f | ge.FLAG_UNFUSED)
@@ -181,7 +188,7 @@ class Workload:
             self.bytes += self.bias.numel() * self.bias.element_size()
         if self.aux is not None:
             self.bytes += self.aux.numel() * self.aux.element_size()
-        self.rotation = None  # list of (A, B, out) for cache-cold decode timing
+        self.rotation = None  # list of (A, B, out) for cache-cold timing of small workloads
 
     def run(self, unfused=False, i=0):
         p = self.unfused if unfused else self.fused
@@ -249,19 +256,31 @@ def build_suite(only):
     suite = []
     t0 = time.time()
     if "c0" in sel:
-        suite.append(Workload("c0_bias", wl.config0_bias()))
+        w = Workload("c0_bias", wl.config0_bias())
+        add_rotation(w, max_copies=80)  # 7 MiB per copy
+        suite.append(w)
     if "c1" in sel:
         for T in (1, 4, 16):
             w = Workload(f"c1_decode_T{T}", wl.config1_decode(T))
             w.rotation = [(w.A, w.B.clone(), torch.empty_like(w.out)) for _ in range(DECODE_COPIES)]
             suite.append(w)
     if "c2" in sel:
-        W1 = W2 = None  # one copy of the FFN weights shared by all token variants
+        # FFN_COPIES copies of both weights (172 MiB each), shared by all token
+        # variants; copy i of the up-projection writes the h that copy i of the
+        # down-projection reads, so the chain stays a chain in every step
+        W1s = W2s = None
         for v in wl.FFN_TOKENS:
             up, down = wl.config2_ffn(v)
-            wu = Workload(f"c2_{v}_up", up, B_dev=W1)
-            wd = Workload(f"c2_{v}_down", down, A_dev=wu.out, B_dev=W2)
-            W1, W2 = wu.B, wd.B
+            wu = Workload(f"c2_{v}_up", up, B_dev=W1s[0] if W1s else None)
+            wd = Workload(f"c2_{v}_down", down, A_dev=wu.out, B_dev=W2s[0] if W2s else None)
+            if W1s is None:
+                W1s = [wu.B] + [wu.B.clone() for _ in range(FFN_COPIES - 1)]
+                W2s = [wd.B] + [wd.B.clone() for _ in range(FFN_COPIES - 1)]
+            xs = [wu.A] + [wu.A.clone() for _ in range(FFN_COPIES - 1)]
+            hs = [wu.out] + [torch.empty_like(wu.out) for _ in range(FFN_COPIES - 1)]
+            ys = [wd.out] + [torch.empty_like(wd.out) for _ in range(FFN_COPIES - 1)]
+            wu.rotation = [(xs[i], W1s[i], hs[i]) for i in range(FFN_COPIES)]
+            wd.rotation = [(hs[i], W2s[i], ys[i]) for i in range(FFN_COPIES)]
             suite += [wu, wd]
     if "c3" in sel:
         for dt in ("f16", "bf16"):
@@ -286,63 +305,148 @@ def time_region(fn, reps, stream):
     return start.elapsed_time(end) / reps  # ms
 
 
+TRIALS = 5
+
+
 def bench_workload(w, reps, stream):
-    """Median of 3 trials of `reps` back-to-back executions, fused and unfused."""
+    """Median and minimum of TRIALS trials of `reps` back-to-back executions,
+    fused and unfused."""
     import statistics
     res = {}
     for label, unf in (("fused", False), ("unfused", True)):
         for i in range(2):
             w.run(unf, i)
-        trials = [time_region(lambda i: w.run(unf, i), reps, stream) for _ in range(3)]
+        trials = [time_region(lambda i: w.run(unf, i), reps, stream) for _ in range(TRIALS)]
         res[label] = statistics.median(trials)
+        res[label + "_min"] = min(trials)
     return res
+
+
+def reps_for(ms_per_call):
+    """Executions per timing trial: at least 200 ms of work, or at least 20
+    executions (and at most 400)."""
+    import math
+    return int(min(400, max(20, math.ceil(200.0 / max(ms_per_call, 1e-4)))))
+
+
+ROTATE_BYTES = 512 << 20  # distinct operand bytes cycled through per small workload
+
+
+def add_rotation(w, max_copies=16):
+    """Cycle a small workload through enough copies of its operands (at least
+    512 MiB together, at most `max_copies`) that each execution reads them
+    from HBM, not from the 256 MB Infinity Cache or the XCDs' L2s."""
+    import math
+    import torch
+    per = w.A.numel() * 2 + w.B.numel() * 2 + w.out.numel() * 2
+    n = int(min(max_copies, max(2, math.ceil(ROTATE_BYTES / per))))
+    w.rotation = [(w.A.clone(), w.B.clone(), torch.empty_like(w.out)) for _ in range(n)]
+    return n
+
+
+def _blas_info(cores):
+    """The BLAS library numpy's fp64 matmul runs on, and its thread count."""
+    try:
+        import threadpoolctl
+        for i in threadpoolctl.threadpool_info():
+            if i.get("user_api") == "blas":
+                return {"library": f"{i.get('internal_api')} {i.get('version')}",
+                        "file": os.path.basename(i.get("filepath", "")),
+                        "threads": int(i.get("num_threads", cores))}
+    except Exception:
+        pass
+    return {"library": "unknown", "file": "", "threads": cores}
+
+
+def _oracle_times(wl, O):
+    """The oracle on each workload's own parity sample, timed once: C0, the
+    T = 16 decode and the 512-token FFN up-projection in full, C3 (fp16) on
+    4096 seed-chosen rows, C4 with the full G that bgrad needs."""
+    out = {}
+
+    def timed(name, flops, fn):
+        t = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t
+        out[name] = {"s": round(dt, 3), "tflops_fp64": round(flops / dt / 1e12, 3)}
+
+    c = wl.config0_bias()
+    timed("c0_bias", 2.0 * c.M * c.N * c.K, lambda: O.gemm_epilogue(
+        c.A, c.B, c.bias, None, c.M, c.N, c.K, c.dtype, c.epilogue, False, False))
+    c = wl.config1_decode(16)
+    timed("c1_decode_T16", 2.0 * c.M * c.N * c.K, lambda: O.gemm_epilogue(
+        c.A, c.B, c.bias, None, c.M, c.N, c.K, c.dtype, c.epilogue, True, True))
+    up, _ = wl.config2_ffn("b1s512")
+    timed("c2_b1s512_up", 2.0 * up.M * up.N * up.K, lambda: O.gemm_epilogue(
+        up.A, up.B, up.bias, None, up.M, up.N, up.K, up.dtype, up.epilogue, True, True))
+    c = wl.config3_relu_aux("f16")
+    rows = wl.sample_rows(c.M, 4096, wl.row_sample_seed(3))
+    A, B = c.host_A(rows), c.host_B()
+    timed("c3_relu_aux_f16_4096_rows", 2.0 * len(rows) * c.N * c.K, lambda: O.gemm_epilogue(
+        A, B, c.bias[rows], None, len(rows), c.N, c.K, "f16", "RELU_AUX_BIAS", False, False))
+    del c, A, B
+    c = wl.config4_drelu_bgrad()
+    A, B = c.host_A(), c.host_B()
+    timed("c4_drelu_bgrad_full_G", 2.0 * c.M * c.N * c.K, lambda: O.gemm_epilogue(
+        A, B, None, c.aux, c.M, c.N, c.K, c.dtype, c.epilogue, False, False,
+        rows=wl.sample_rows(c.M, 4096, wl.row_sample_seed(4))))
+    del c, A, B
+    return out
 
 
 def cpu_baseline(seconds_target=12.0):
     """The oracle, as it stands, on a bounded sample of the C3 workload
     (fp16): seed-chosen output rows against the full B, sized to about
-    `seconds_target` seconds of host work."""
-    import numpy as np
+    `seconds_target` seconds of host work; with its BLAS threads pinned to
+    the host cores this process may use.  Also the oracle's time on each
+    workload's own parity sample."""
     import torch
     import workloads as wl
     from oracle import oracle as O
     cores = len(os.sched_getaffinity(0))
-    c = wl.config3_relu_aux("f16")
-    B = c.host_B()
-    rows_all = wl.sample_rows(c.M, 32768, wl.row_sample_seed(3))
-    # calibrate: a small warm-up call (thread pools, page faults), then a
-    # 4096-row probe; size the timed sample to ~seconds_target from the probe
-    def run(rs):
-        A_rs = c.host_A(rs)
-        t = time.perf_counter()
-        O.gemm_epilogue(A_rs, B, c.bias[rs], None, len(rs), c.N, c.K, "f16",
-                        "RELU_AUX_BIAS", False, False)
-        return time.perf_counter() - t
-    run(rows_all[:32])
-    # fp64 matmul throughput still rises with the row count at this size,
-    # so the probe is large (about a second) and the estimate conservative
-    probe = 4096
-    dt = run(rows_all[:probe])
-    nrows = int(max(probe, min(len(rows_all), probe * seconds_target / max(dt, 1e-3))))
-    rows = rows_all[:nrows]
-    A_rows = c.host_A(rows)
-    t = time.perf_counter()
-    O.gemm_epilogue(A_rows, B, c.bias[rows], None, len(rows), c.N, c.K, "f16", "RELU_AUX_BIAS",
-                    False, False)
-    dt = time.perf_counter() - t
-    del c
-    torch.cuda.empty_cache()
-    flops = 2.0 * len(rows) * 8192 * 16384
     try:
         import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max((i.get("num_threads", 1) for i in info), default=cores)
+        limiter = threadpoolctl.threadpool_limits(limits=cores, user_api="blas")
     except Exception:
-        threads = cores
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+        limiter = None
+    try:
+        c = wl.config3_relu_aux("f16")
+        B = c.host_B()
+        rows_all = wl.sample_rows(c.M, 32768, wl.row_sample_seed(3))
+
+        # calibrate: a small warm-up call (thread pools, page faults), then a
+        # 4096-row probe; size the timed sample to ~seconds_target from the probe
+        def run(rs):
+            A_rs = c.host_A(rs)
+            t = time.perf_counter()
+            O.gemm_epilogue(A_rs, B, c.bias[rs], None, len(rs), c.N, c.K, "f16",
+                            "RELU_AUX_BIAS", False, False)
+            return time.perf_counter() - t
+        run(rows_all[:32])
+        # fp64 matmul throughput still rises with the row count at this size,
+        # so the probe is large (about a second) and the estimate conservative
+        probe = 4096
+        dt = run(rows_all[:probe])
+        nrows = int(max(probe, min(len(rows_all), probe * seconds_target / max(dt, 1e-3))))
+        rows = rows_all[:nrows]
+        A_rows = c.host_A(rows)
+        t = time.perf_counter()
+        O.gemm_epilogue(A_rows, B, c.bias[rows], None, len(rows), c.N, c.K, "f16",
+                        "RELU_AUX_BIAS", False, False)
+        dt = time.perf_counter() - t
+        del c, A_rows, B
+        torch.cuda.empty_cache()
+        per_config = _oracle_times(wl, O)
+        blas = _blas_info(cores)
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
+    flops = 2.0 * len(rows) * 8192 * 16384
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas["threads"]),
+            "kind": "oracle", "host_cores": cores, "blas": blas, "per_config": per_config,
             "sample": f"C3 fp16 RELU_AUX_BIAS, {len(rows)} sampled rows of 65536 "
-                      f"(x 8192 cols, K=16384; fp64 numpy), {dt:.1f} s, host cores {cores}"}
+                      f"(x 8192 cols, K=16384; fp64 numpy matmul, {blas['library']}, "
+                      f"{blas['threads']} threads), {dt:.1f} s, host cores {cores}"}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c3_relu_aux_f16.json")
@@ -454,6 +558,27 @@ def profile_decode():
         torch.cuda.empty_cache()
 
 
+def profile_workloads(only):
+    """The 1 GiB copy (the FETCH/WRITE calibration), then two fused executions
+    of each selected suite workload in turn (rotated copies as in the
+    timing), each workload's plan printed first."""
+    import torch
+    n = 1 << 29
+    src = torch.empty(n, dtype=torch.float16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    suite = build_suite(only or "c0,c2,c4")
+    for w in suite:
+        log(f"profile-workloads {w.name}: {w.fused.info()}")
+        for i in range(2):
+            w.run(False, i)
+        torch.cuda.synchronize()
+
+
 def compare_blas(only, trials=5):
     """Context for the roofline figures: the vendor BLAS on the same shapes.
 
@@ -544,7 +669,7 @@ def main():
         torch.cuda.set_device(0)
         compare_blas(args.only)
         return
-    if args.profile_traffic or args.profile_decode or args.profile_layouts:
+    if args.profile_traffic or args.profile_decode or args.profile_layouts or args.profile_workloads:
         import torch  # noqa: F401
         import activation_epilogue_gemm_amd as ge
         ge.library()
@@ -552,6 +677,8 @@ def main():
             profile_traffic()
         elif args.profile_layouts:
             profile_layouts()
+        elif args.profile_workloads:
+            profile_workloads(args.only)
         else:
             profile_decode()
         return
@@ -620,10 +747,12 @@ def main():
         reps = args.reps
         if not reps:
             t = time_region(lambda i: w.run(False, i), 3, stream)
-            reps = int(max(5, min(200, 150.0 / max(t, 1e-3))))
+            reps = reps_for(t)
         r = bench_workload(w, reps, stream)
         f_ms, u_ms = r["fused"], r["unfused"]
         entry = {"fused_ms": round(f_ms, 5), "unfused_ms": round(u_ms, 5),
+                 "fused_min_ms": round(r["fused_min"], 5), "unfused_min_ms": round(r["unfused_min"], 5),
+                 "trials": TRIALS, "rotated_copies": len(w.rotation) if w.rotation else 1,
                  "speedup": round(u_ms / f_ms, 4), "reps": reps,
                  "tflops": round(w.flops / f_ms / 1e9, 2),
                  "frac_mfma_peak": round(w.flops / f_ms / 1e9 / PEAK_TFLOPS, 4),
@@ -671,6 +800,8 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic,
                 "kernel": dom.name, "avg_launch_ms": round(ms, 5), "launches": len(dom_events),
+                "bracket": ("the workload's execution: the B staging copy, then the GEMM kernel"
+                            if "stage_b" in dom.fused.info() else "the GEMM kernel"),
                 "algorithmic_bytes": dom.bytes, "kernel_source_sha": kernel_source_hash(),
                 "frac_of_clock_adjusted_peak": util,
                 "implied_sclk_mhz": round(sclk) if sclk else None}

@@ -160,3 +160,28 @@ def test_flag_chosen_split_on_the_small_workloads(case):
             c.A = oracle_of(up).out
     for flags in (ge.FLAG_SPLIT_K, ge.FLAG_SPLIT_K | ge.FLAG_UNFUSED):
         run_and_check(c, None, flags=flags, label=case)
+
+
+def test_split_k_arrivals_over_many_rounds():
+    """The arrival protocol (partials written with agent-scope stores, a
+    relaxed counter increment after a barrier, the last arriver's
+    agent-scope loads) rests on the hardware making a workgroup's completed
+    agent-scope stores visible to a workgroup on another XCD that observes
+    its counter increment.  Here it is exercised on a grid far larger than
+    one round of the chip: 4096 output tiles of 64 x 64, each split 8 ways
+    (32768 workgroups, 128 rounds of 256 CUs), integer inputs, every result
+    bit-exact, three executions in a row on one workspace."""
+    import torch
+    M, N, K = 4096, 4096, 1024
+    c = wl.random_case(M, N, K, "f16", "BIAS", False, False, 3900, kind="int")
+    r = GpuRun(c, tile=5, splits=8)
+    say("many rounds", r.info)
+    assert "splits=8" in r.info
+    ref = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, "f16", "BIAS", False, False)
+    for rep in range(3):
+        r.out.view(torch.int16).fill_(0x7E00)
+        r.run()
+        got = r.out_bits()
+        assert np.array_equal(got, ref.out), \
+            f"execution {rep}: {int((got != ref.out).sum())} elements differ"
+    r.close()

@@ -154,7 +154,10 @@ gemmepi_status_t gemmepi_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_
  * As gemmepi_plan, with an explicit tile configuration of the tiled GEMM
  * (0 <= tile_id < gemmepi_num_tiles(); -1 = heuristic choice, identical to
  * gemmepi_plan).  Used by tuning sweeps and by tests that cover every tile
- * shape.  An explicit tile_id also disables the decode kernel.
+ * shape.  An explicit tile_id also disables the decode kernel.  The pages'
+ * planner picks one of several algorithm candidates for a shape; this call
+ * fixes the candidate instead ("nvmath-python cuBLASLt bias fusion guide",
+ * section "Advanced techniques and engineering practice").
  * Errors: as gemmepi_plan, plus INVALID_VALUE for an unknown tile_id.
  */
 gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
@@ -168,7 +171,10 @@ gemmepi_status_t gemmepi_plan_tiled(gemmepi_plan_t* plan, int64_t M, int64_t N, 
  * workspace, and the last range of a tile to finish sums the partials in
  * range order (so out does not depend on which finishes last) and applies
  * the epilogue once.  This is the wave-quantisation remedy for shapes with
- * few output tiles and a long K.
+ * few output tiles and a long K; the pages do not define it.  Its
+ * caller-owned workspace follows the workspace argument the pages pass to
+ * the vendor library's matmul ("Bias fusion with cuBLASLt in PyTorch
+ * inference: fewer kernel launches and memory accesses", body).
  *
  *   splits  1 = no split; 2 .. 64 = that many ranges (fewer when K has
  *           fewer k slabs of the tile); 0 = chosen by plan() with the tile
@@ -183,8 +189,10 @@ gemmepi_status_t gemmepi_plan_split(gemmepi_plan_t* plan, int64_t M, int64_t N, 
                                     uint32_t flags, int32_t tile_id, int32_t splits);
 
 /*
- * Device workspace a plan needs, in bytes: 0 unless the plan stages B or
- * splits K.  A staged plan needs 2 N K bytes (padded to 256) for the copy of
+ * Device workspace a plan needs, in bytes (the caller-owned workspace of
+ * the vendor library's matmul in "Bias fusion with cuBLASLt in PyTorch
+ * inference: fewer kernel launches and memory accesses", body): 0 unless
+ * the plan stages B or splits K.  A staged plan needs 2 N K bytes (padded to 256) for the copy of
  * B; a split plan 4 bytes per output tile (arrival counters, padded to 256
  * bytes) plus one fp32 partial tile per (tile, split).  NULL plan: 0.
  */
@@ -344,36 +352,50 @@ gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const 
                                       void* stats, void* out, void* stream);
 
 /* Bytes of the stats buffer of gemmepi_execute_norm for M rows (16 M);
- * 0 for M < 1. */
+ * 0 for M < 1.  The statistics of the MatMul + Norm operator of the ops-nn
+ * MatMul fusion article, section "Level 2: structural fusion". */
 size_t gemmepi_norm_stats_bytes(int64_t M);
 
-/* Drop one reference; the plan is freed when the last reference goes.
+/* Drop one reference; the plan is freed when the last reference goes: the
+ * release of the Matmul object's resources ("Fusing bias addition with
+ * matrix multiplication using nvmath-python", paragraph 5).
  * Errors: INVALID_VALUE for NULL or a handle that is not live. */
 gemmepi_status_t gemmepi_plan_destroy(gemmepi_plan_t plan);
 
 /* Human-readable description of the plan (path, tile, grid) into buf
- * (NUL-terminated, truncated to len).  Errors: INVALID_VALUE. */
+ * (NUL-terminated, truncated to len): which candidate the planner chose
+ * ("nvmath-python cuBLASLt bias fusion guide", section "Advanced techniques
+ * and engineering practice").  Errors: INVALID_VALUE. */
 gemmepi_status_t gemmepi_plan_info(gemmepi_plan_t plan, char* buf, size_t len);
 
 /* Number of tile configurations of the tiled GEMM, and the name
- * ("BMxBNxBK_wWMxWN") of one of them (NULL for an unknown id). */
+ * ("BMxBNxBK_wWMxWN_sNS_pSCHED_mMFMA") of one of them (NULL for an unknown
+ * id): the algorithm candidates the planner chooses among ("nvmath-python
+ * cuBLASLt bias fusion guide", section "Advanced techniques and engineering
+ * practice"). */
 int32_t gemmepi_num_tiles(void);
 const char* gemmepi_tile_name(int32_t tile_id);
 
 /* Mask row pitch in uint32 words for N columns: ceil(N/32) rounded up to a
  * multiple of 4 (16 bytes); and the mask size in bytes for M rows.
- * Return 0 for N < 1 (or M < 1). */
+ * Return 0 for N < 1 (or M < 1).  The mask is the ReLU auxiliary output of
+ * "Fusing bias addition with matrix multiplication using nvmath-python",
+ * paragraph 4, which gives no layout; this bit-packed one is the library's. */
 int64_t gemmepi_aux_ld_words(int64_t N);
 size_t gemmepi_aux_bytes(int64_t M, int64_t N);
 
-/* Static string for a status code ("unknown status" for others). */
+/* Static string for a status code ("unknown status" for others): the
+ * library's form of the runtime error the pages raise for invalid operands
+ * ("Fusing bias addition with matrix multiplication using nvmath-python",
+ * paragraph 5). */
 const char* gemmepi_status_string(gemmepi_status_t s);
 
 /* Thread-local description of the most recent failure in this thread
  * ("" if none).  Valid until the next failing call in the same thread. */
 const char* gemmepi_last_error(void);
 
-/* GEMMEPI_VERSION of the built library. */
+/* GEMMEPI_VERSION of the built library (library bookkeeping; no passage of
+ * the pages defines it). */
 int32_t gemmepi_version(void);
 
 

@@ -161,6 +161,28 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
 // (each vector element is copied to a scalar before the bit cast: this
 // compiler's __builtin_bit_cast of an ext_vector element expression reads
 // element 0 whatever the index)
+// Sum of v over the 64 lanes of a wave, left in lane 63 (other lanes hold
+// partial sums).  DPP moves within rows of 16 lanes (quad permutations, then
+// the half-row and row mirrors) leave every lane with its row's sum; the row
+// broadcasts of lane 15 and lane 31 then fold rows 0..2 into row 3.  Each
+// step is a VALU operation with a DPP source, a few cycles, where a
+// cross-lane shuffle through the LDS crossbar costs an LDS round trip.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, RowMask, 0xF,
+                                                false);
+  return v + __builtin_bit_cast(float, moved);
+}
+__device__ __forceinline__ float wave_sum_to_lane63(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 __device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float c, _Float16) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -188,6 +210,15 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
   const int wave = tid >> 6;
   const int n0 = blockIdx.x * R;
   const int Mt = p.M;
+  // the epilogue lane's bias value (wave 0, lane = r * TB + t) is requested
+  // before the weight stream, so its latency is not added after the
+  // reduction; out-of-range entries read zero
+  const int er = lane / TB, et = lane - (lane / TB) * TB;
+  const bool want_bias = wave == 0 && lane < R * TB && p.epi != EPI_DEFAULT && et < Mt &&
+                         (!p.bias_per_col || n0 + er < p.N);
+  const __amdgpu_buffer_rsrc_t rBias = make_rsrc(p.bias ? p.bias : p.W);
+  const uint16_t braw = __builtin_amdgcn_raw_buffer_load_b16(
+      rBias, want_bias ? (uint32_t)(p.bias_per_col ? n0 + er : et) * 2u : kOOB, 0, 0);
   const __amdgpu_buffer_rsrc_t rW = make_rsrc((const uint8_t*)p.W + (size_t)n0 * p.ldw * 2);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(p.x);
   float acc[R][TB];
@@ -216,13 +247,8 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      float v = acc[r][t];
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-      acc[r][t] = v;
-    }
-  if (lane == 0) {
+    for (int t = 0; t < TB; ++t) acc[r][t] = wave_sum_to_lane63(acc[r][t]);
+  if (lane == 63) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -230,20 +256,16 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
   }
   __syncthreads();
   if (wave != 0 || lane >= R * TB) return;
-  const int r = lane / TB, t = lane - (lane / TB) * TB;
-  const int n = n0 + r;
-  if (n >= p.N || t >= Mt) return;
+  const int n = n0 + er;
+  if (n >= p.N || et >= Mt) return;
   float z = 0.0f;
 #pragma unroll
   for (int w = 0; w < kDecodeWaves; ++w) z += red[w][lane];
-  if (p.epi != EPI_DEFAULT) {
-    const T* bias = (const T*)p.bias;
-    z += to_f32(bias[p.bias_per_col ? n : t]);
-  }
+  if (p.epi != EPI_DEFAULT) z += to_f32(__builtin_bit_cast(T, braw));
   float y = z;
   if (p.epi == EPI_GELU_BIAS) y = gelu_erf(z);
   else if (p.epi == EPI_RELU_BIAS) y = z > 0.0f ? z : 0.0f;
-  ((T*)p.out)[(size_t)t * p.ldo + n] = from_f32<T>(y);
+  ((T*)p.out)[(size_t)et * p.ldo + n] = from_f32<T>(y);
 }
 
 // Rows per workgroup of the row-streaming kernel for M tokens; 0: the MFMA

@@ -626,7 +626,9 @@ def compare_blas(only, trials=5):
             flags = ge.FLAG_SPLIT_K | ge.FLAG_B_TRANS | (ge.FLAG_BIAS_PER_COL if c.bias_per_col else 0)
             w.fused = ge.plan(c.M, c.N, c.K, c.dtype, c.epilogue, flags)
             w.B = B
-        f = ge.FLAG_SPLIT_K | (ge.FLAG_B_TRANS if b_trans else 0)
+        # the plain GEMM takes the fused plan's path (split, staged B) with
+        # the DEFAULT epilogue
+        f = ge.FLAG_SPLIT_K | ge.FLAG_STAGE_B | (ge.FLAG_B_TRANS if b_trans else 0)
         plain = ge.plan(c.M, c.N, c.K, c.dtype, "DEFAULT", f)
         scratch = torch.empty_like(w.out)
         Bop = B.t() if b_trans else B

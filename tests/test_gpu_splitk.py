@@ -162,6 +162,25 @@ def test_flag_chosen_split_on_the_small_workloads(case):
         run_and_check(c, None, flags=flags, label=case)
 
 
+def test_first_execution_enqueued_on_another_stream():
+    """The binding allocates a split plan's workspace at its first execution
+    and zeroes it on torch's current stream; an execution enqueued on a
+    different stream (passed explicitly, not made current) must still find
+    the arrival counters at zero, or no range would run the epilogue and the
+    output would be left as it was."""
+    import torch
+    c = wl.random_case(300, 264, 600, "f16", "RELU_BIAS", False, False, 3950, kind="int")
+    r = GpuRun(c, tile=5, splits=3)
+    s = torch.cuda.Stream()
+    r.out.view(torch.int16).fill_(0x7E00)
+    torch.cuda.synchronize()
+    r.plan.execute(r.A, r.B, r.bias, r.aux, r.out, stream=s)
+    s.synchronize()
+    ref = oracle_of(c)
+    assert np.array_equal(r.out_bits(), ref.out)
+    r.close()
+
+
 def test_split_k_arrivals_over_many_rounds():
     """The arrival protocol (partials written with agent-scope stores, a
     relaxed counter increment after a barrier, the last arriver's

@@ -270,7 +270,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
 
 // Rows per workgroup of the row-streaming kernel for M tokens; 0: the MFMA
 // decode kernel above.  Measured over the 16 rotated 4096 x 4096 weights
-// against the MFMA kernel: 4 rows 7.96 against 8.44 us at M = 1, 8.43
+// against the MFMA kernel: 4 rows 7.54 against 8.44 us at M = 1, 7.73
 // against 8.78 at M = 2, but 12.6 against 8.8 at M = 4 (each workgroup
 // re-reads every token row, 32 MiB in all, and the VALU products grow
 // with M); 8 rows per workgroup were slower at every M.

@@ -139,6 +139,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // carries the immediate offset 1024 g, which the hardware adds to both the
 // LDS and the global address, so voff[g] must be the global offset of block
 // g minus 1024 g (or an out-of-range offset, which reads zero).
+// The output tile's 16-byte row stores carry the non-temporal hint (1) or
+// are ordinary stores (0).  The output is written once and not read again
+// by the kernel; with the hint it displaces less of the operands' cached
+// panels.  Measured inside the benchmark suite (cold operands, one box,
+// runs alternated): the FFN GEMMs 1.5-4 % faster, C3 bf16 1 %, C4 0.2 %,
+// C3 fp16 0.3 % slower (within its run-to-run spread).
+#ifndef GEMMEPI_NT_OUT
+#define GEMMEPI_NT_OUT 1
+#endif
+
 #ifndef GEMMEPI_M0_GROUPS
 #define GEMMEPI_M0_GROUPS 0
 #endif
@@ -1279,7 +1289,10 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       if (m >= M || n >= N) continue;
       T* dst = dst_base + (size_t)m * ldo + n;
       if (vec_store && n + 7 < N) {
-        *(u32x4*)dst = v;
+        if constexpr (GEMMEPI_NT_OUT)
+          __builtin_nontemporal_store(v, (u32x4*)dst);
+        else
+          *(u32x4*)dst = v;
       } else {
         uint16_t* d16 = (uint16_t*)dst;
 #pragma unroll

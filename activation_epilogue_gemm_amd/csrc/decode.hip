@@ -37,9 +37,14 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // Cache policy of the weight loads (the aux operand of the buffer load):
-// 0 = normal, 2 = non-temporal (streamed, evict-first in L2).
+// 0 = normal, 2 = non-temporal (streamed, evict-first in L2).  The weight
+// is read once per call.  Measured over 16 rotated 4096 x 4096 weights,
+// interleaved on one box, non-temporal against normal: 6.95 against 7.55 us
+// at one token, 7.21 against 7.71 at two, 9.16 against 9.61 at eight, 10.46
+// against 10.59 at sixteen, but 8.93 against 8.85 at four, so the MFMA
+// kernel streams non-temporally from 8 tokens on.
 #ifndef GEMMEPI_DECODE_W_POLICY
-#define GEMMEPI_DECODE_W_POLICY 0
+#define GEMMEPI_DECODE_W_POLICY 2
 #endif
 
 constexpr int kDecodeWaves = 8;
@@ -58,6 +63,7 @@ __device__ __forceinline__ uint32_t xwin_off(int t, int chunk) {
 template <typename T, int TB>
 __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeArgs p) {
   using V8 = typename Frag<T>::type;
+  constexpr int kWPolicy = TB >= 8 ? GEMMEPI_DECODE_W_POLICY : 0;
   __shared__ f32x4 red[kDecodeWaves][64];
   __shared__ __attribute__((aligned(16))) uint8_t xwin[kDecodeWaves][TB * kDecodeWin * 2];
 
@@ -107,7 +113,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
     for (int u = 0; u < kDecodeUnroll; ++u) {
       const int kk = k + u * 32 + kg * 8;
       wv[u] = __builtin_amdgcn_raw_buffer_load_b128(
-          rW, (kk < kend && w_ok) ? w_row + (uint32_t)kk * 2u : kOOB, 0, GEMMEPI_DECODE_W_POLICY);
+          rW, (kk < kend && w_ok) ? w_row + (uint32_t)kk * 2u : kOOB, 0, kWPolicy);
     }
 #pragma unroll
     for (int t = 0; t < TB; ++t) *(u32x4*)(xw + xwin_off(t, lane)) = xl[t];
@@ -270,10 +276,11 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
 
 // Rows per workgroup of the row-streaming kernel for M tokens; 0: the MFMA
 // decode kernel above.  Measured over the 16 rotated 4096 x 4096 weights
-// against the MFMA kernel: 4 rows 7.54 against 8.44 us at M = 1, 7.73
-// against 8.78 at M = 2, but 12.6 against 8.8 at M = 4 (each workgroup
-// re-reads every token row, 32 MiB in all, and the VALU products grow
-// with M); 8 rows per workgroup were slower at every M.
+// against the MFMA kernel (normal weight loads): 4 rows 7.54 against
+// 8.44 us at M = 1, 7.73 against 8.78 at M = 2, but 12.6 against 8.8 at
+// M = 4 (each workgroup re-reads every token row, 32 MiB in all, and the
+// VALU products grow with M); 8 rows per workgroup were slower at every M,
+// 2 rows no faster with non-temporal weight loads.
 #ifndef GEMMEPI_GEMV_ROWS
 #define GEMMEPI_GEMV_ROWS 4
 #endif

@@ -276,15 +276,17 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
 
 // Rows per workgroup of the row-streaming kernel for M tokens; 0: the MFMA
 // decode kernel above.  Measured over the 16 rotated 4096 x 4096 weights
-// against the MFMA kernel (normal weight loads): 4 rows 7.54 against
-// 8.44 us at M = 1, 7.73 against 8.78 at M = 2, but 12.6 against 8.8 at
-// M = 4 (each workgroup re-reads every token row, 32 MiB in all, and the
+// against the MFMA kernel, interleaved on one box: 4 rows (bias requested
+// first, DPP reduction, non-temporal weight loads) 6.95 against 8.44 us at
+// M = 1, 7.21 against 8.78 at M = 2, 7.96 against 8.78 at M = 3 and 8.18
+// against 8.81 at M = 4, but 13.1-13.9 against 9.1-9.2 at M = 5..8 (each
+// workgroup re-reads every token row, 64 MiB in all at 8 tokens, and the
 // VALU products grow with M); 8 rows per workgroup were slower at every M,
-// 2 rows no faster with non-temporal weight loads.
+// 2 rows no faster.
 #ifndef GEMMEPI_GEMV_ROWS
 #define GEMMEPI_GEMV_ROWS 4
 #endif
-int gemv_rows(int M) { return M <= 2 ? GEMMEPI_GEMV_ROWS : 0; }
+int gemv_rows(int M) { return M <= 4 ? GEMMEPI_GEMV_ROWS : 0; }
 
 template <typename T>
 static void launch_gemv_t(const DecodeArgs& a, int R, hipStream_t s) {
@@ -296,7 +298,8 @@ static void launch_gemv_t(const DecodeArgs& a, int R, hipStream_t s) {
     else GEMMEPI_GEMV(8, 2);
   } else {
     if (a.M <= 1) GEMMEPI_GEMV(4, 1);
-    else GEMMEPI_GEMV(4, 2);
+    else if (a.M <= 2) GEMMEPI_GEMV(4, 2);
+    else GEMMEPI_GEMV(4, 4);
   }
 #undef GEMMEPI_GEMV
 }

@@ -128,7 +128,7 @@ def test_unfused_matches_oracle(epi, dtype):
 
 
 # ---------------------------------------------------------------- decode path
-@pytest.mark.parametrize("T", [1, 2, 4, 7, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 7, 16])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_decode_path(T, dtype):
     for epi in ("DEFAULT", "BIAS", "RELU_BIAS", "GELU_BIAS"):

@@ -151,8 +151,8 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
   }
 }
 
-// ---- row-streaming decode for one or two tokens --------------------------
-// With M <= 2 the products are too few to need the matrix cores, and the
+// ---- row-streaming decode for one to four tokens -------------------------
+// With M <= 4 the products are too few to need the matrix cores, and the
 // weight stream is best read the way a plain streaming read is fastest: one
 // contiguous 1 KiB per load instruction, and many small workgroups (the
 // stream-read sweep of the benchmark peaks at 32 KiB per workgroup).  A
@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
 // 16 bytes there and the wave's 64 lanes read 1 KiB of one row.  Each lane
 // multiplies its W chunks with the same k chunk of every token on the VALU
 // (v_dot2: fp32 accumulation of exact fp16/bf16 products), the R x TB
-// partial sums are reduced over the wave's lanes by a butterfly, then over
+// partial sums are reduced over the wave's lanes (DPP, below), then over
 // the 8 waves through LDS, and wave 0 applies the epilogue.
 // (each vector element is copied to a scalar before the bit cast: this
 // compiler's __builtin_bit_cast of an ext_vector element expression reads

@@ -50,6 +50,7 @@ FLAG_VALIDATE = 1 << 3
 FLAG_NO_DECODE = 1 << 4
 FLAG_SPLIT_K = 1 << 5
 FLAG_STAGE_B = 1 << 6
+FLAG_NORM_TWO_PASS = 1 << 7
 
 
 class GemmEpiError(RuntimeError):
@@ -274,7 +275,9 @@ class Plan:
                      gamma: Pointer, beta: Pointer, eps: float, stats: Pointer, out: Pointer,
                      stream=None, check: bool = True) -> None:
         """Enqueue one GEMM + bias + residual + row-norm execution
-        (gemmepi_execute_norm); stats is an fp64 [M, 2] tensor."""
+        (gemmepi_execute_norm).  stats is an fp64 tensor of
+        norm_stats_bytes(M) / 8 elements (norm_stats_buffer); on return its
+        first 2 M elements are (mean, rstd) per row."""
         if self._h is None:
             raise ValueError("plan destroyed")
         if check:
@@ -383,7 +386,8 @@ class Plan:
         for t, name, dtype, numel in ((A, "A", tdt, M * K), (B, "B", tdt, N * K),
                                       (out, "out", tdt, M * N), (bias, "bias", tdt, N),
                                       (residual, "residual", tdt, M * N), (gamma, "gamma", tdt, N),
-                                      (beta, "beta", tdt, N), (stats, "stats", torch.float64, 2 * M)):
+                                      (beta, "beta", tdt, N),
+                                      (stats, "stats", torch.float64, norm_stats_bytes(M) // 8)):
             if t is None or isinstance(t, int):
                 continue
             if not isinstance(t, torch.Tensor):
@@ -407,7 +411,31 @@ def noalloc_scratch_bytes() -> int:
 
 
 def norm_stats_bytes(M: int) -> int:
+    """gemmepi_norm_stats_bytes: bytes of execute_norm's stats buffer."""
     return int(_load().gemmepi_norm_stats_bytes(M))
+
+
+def norm_stats_buffer(M: int, device="cuda"):
+    """A stats buffer for execute_norm on M rows: an fp64 tensor of
+    norm_stats_bytes(M) / 8 elements.  After an execution, mean and rstd of
+    row m are elements 2 m and 2 m + 1 (norm_mean_rstd); the 32-bit word
+    after them is 1 after a single-pass execution, 0 after two kernels
+    (norm_pass_status)."""
+    import torch
+    return torch.zeros(norm_stats_bytes(M) // 8, dtype=torch.float64, device=device)
+
+
+def norm_mean_rstd(stats, M: int):
+    """The [M, 2] (mean, rstd) view of an execute_norm stats buffer."""
+    return stats[: 2 * M].view(M, 2)
+
+
+def norm_pass_status(stats, M: int) -> int:
+    """The status word of an execute_norm stats buffer (copied to the
+    host): bit 0 set after a single pass, bit 1 set if a workgroup of it
+    stopped waiting for its band of rows."""
+    import torch
+    return int(stats[4 * M: 4 * M + 1].view(torch.int32)[0].item())
 
 
 def plan(M: int, N: int, K: int, dtype: str = "f16", epilogue: str = "BIAS", flags: int = 0,

@@ -8,4 +8,8 @@ hipError_t launch_gemm_f16_bn(int tile, const GemmArgs& a, hipStream_t s) {
   return launch_by_tile<_Float16, false>(tile, a, s);
 }
 
+hipError_t blocks_per_cu_f16_bn(int tile, int* n) {
+  return blocks_per_cu_by_tile<_Float16, false>(tile, n);
+}
+
 }  // namespace gemmepi

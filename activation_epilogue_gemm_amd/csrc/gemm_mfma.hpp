@@ -64,6 +64,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Out-of-range voffset: larger than the descriptor's record count, so the
 // buffer load returns zeros.
 constexpr uint32_t kOOB = 0x80000000u;
+// Polls of the single-pass norm's row wait before a workgroup gives up
+// (each poll: one device-coherent load and a ~128-cycle sleep; the bound is
+// in the seconds, where a normal wait lasts microseconds).
+constexpr uint32_t kNormWaitPolls = 1u << 21;
 constexpr int kNumRecords = 0x7FFFFFFF;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -368,7 +372,9 @@ struct GemmTile {
   // ([WN][BM][2] fp64 partial row sums for the norm epilogue)
   static constexpr int OUT_BYTES = BM * BN * 2;
   static constexpr int RED_BYTES = WM * BN * 4 > BM * WN * 16 ? WM * BN * 4 : BM * WN * 16;
-  static constexpr int BIAS_BYTES = (BM > BN ? BM : BN) * 4;  // the tile's bias slice, fp32
+  // the tile's bias slice (BM or BN fp32), or for the single-pass norm its
+  // bias, gamma and beta slices (3 BN fp32), and a flag word
+  static constexpr int BIAS_BYTES = (BM > 3 * BN ? BM : 3 * BN) * 4 + 16;
   static constexpr int EPI_BYTES = OUT_BYTES + RED_BYTES + BIAS_BYTES;
   static constexpr int SMEM = NS * STAGE > EPI_BYTES ? NS * STAGE : EPI_BYTES;
   static_assert(SMEM <= 160 * 1024, "LDS");
@@ -1133,6 +1139,167 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
         for (int r = 0; r < kAccN; ++r)
           red[wm * BN + wcol0 + fn * kMfma + kColStride * (r >> 2) + 4 * lgrp + (r & 3)] = cs[fn][r];
     }
+  } else if (epi == EPI_BIAS_RES_NORM) {
+    // Single-pass GEMM + bias + residual + norm.  y = acc + bias + residual
+    // is formed in fp32 from the accumulators (never rounded before the
+    // norm), once for the row sums and again, bit for bit the same, for the
+    // normalisation (the accumulators stay unchanged, so no second copy of
+    // the tile is held in registers; the residual stays staged in LDS until
+    // each lane overwrites its own elements with the result).
+    // The row sums of y and y^2 of the whole row (all tiles_n workgroups of
+    // this tile row) meet in fp64 in row_sums: each workgroup adds its
+    // partial sums, then counts its arrival; when all have arrived, each
+    // reads the row statistics, normalises its own tile and writes it once.
+    // The host runs this form only when the whole grid fits on the chip at
+    // once, so every workgroup of the tile row is resident and the wait
+    // ends; the wait is still bounded, and a workgroup that gives up sets
+    // bit 1 of row_sync[0] and writes NaN rows.
+    load_tile((const T*)p.residual);
+    float* const gsl = bsl + BN;      // gamma slice
+    float* const esl = bsl + 2 * BN;  // beta slice
+    uint32_t* const wait_ok = (uint32_t*)(bsl + 3 * BN);
+    const bool has_beta = p.beta != nullptr;
+    {
+      const T* bias = (const T*)p.bias;
+      const T* gamma = (const T*)p.gamma;
+      const T* beta = (const T*)p.beta;
+      for (int i = tid; i < BN; i += NT) {
+        const bool in = n0 + i < N;
+        bsl[i] = (bias != nullptr && in) ? to_f32(bias[n0 + i]) : 0.0f;
+        gsl[i] = in ? to_f32(gamma[n0 + i]) : 0.0f;
+        esl[i] = (has_beta && in) ? to_f32(beta[n0 + i]) : 0.0f;
+      }
+    }
+    __syncthreads();
+    double* red64 = (double*)(smem + G::OUT_BYTES);  // [WN][BM][2]
+    static_for<FM>([&](auto fm_c) {
+      constexpr int fm = decltype(fm_c)::value;
+      // one row block at a time: interleaving them would hold the LDS reads
+      // of all blocks in registers beside the live accumulators
+      __builtin_amdgcn_sched_barrier(0);
+      const int rl = wrow0 + fm * kMfma + lrow;
+      const int m = m0 + rl;
+      double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int cl = wcol0 + fn * kMfma + 4 * lgrp;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const int c_loc = cl + kColStride * g;
+          const u32x2 rw = *(const u32x2*)staged4(rl, c_loc);
+          const f32x4 b4 = *(const f32x4*)(bsl + c_loc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint16_t rb = (uint16_t)(rw[e >> 1] >> (16 * (e & 1)));
+            const float y = acc[fm][fn][4 * g + e] + b4[e] + to_f32(__builtin_bit_cast(T, rb));
+            if (n0 + c_loc + e < N && m < M) {
+              s1 += (double)y;
+              s2 += (double)y * (double)y;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int o = kMfma; o < 64; o <<= 1) {
+        s1 += __shfl_xor(s1, o);
+        s2 += __shfl_xor(s2, o);
+      }
+      if (lgrp == 0) {
+        red64[(wn * BM + rl) * 2] = s1;
+        red64[(wn * BM + rl) * 2 + 1] = s2;
+      }
+    });
+    __syncthreads();
+    for (int r = tid; r < BM; r += NT) {
+      const int m = m0 + r;
+      if (m >= M) continue;
+      double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+      for (int w = 0; w < WN; ++w) {
+        s1 += red64[(w * BM + r) * 2];
+        s2 += red64[(w * BM + r) * 2 + 1];
+      }
+      unsafeAtomicAdd(&p.row_sums[2 * (size_t)m], s1);
+      unsafeAtomicAdd(&p.row_sums[2 * (size_t)m + 1], s2);
+    }
+    // every thread's sums have reached the device-coherent level before
+    // thread 0 counts this workgroup in (as in the split-K arrival)
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t* const arrived = p.row_sync + 1 + tm;
+      __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t ok = 1u;
+      for (uint32_t polls = 0;
+           __hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.tiles_n;
+           ++polls) {
+        if (polls >= kNormWaitPolls) {
+          ok = 0u;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (tm == 0 && tn == 0) __hip_atomic_fetch_or(p.row_sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!ok) __hip_atomic_fetch_or(p.row_sync, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *wait_ok = ok;
+    }
+    __syncthreads();
+    const bool ok = *wait_ok != 0u;
+    // row statistics in fp64 from the complete sums (the red64 slots are
+    // free again: every read of them preceded the last barrier)
+    float* const msl = (float*)(smem + G::OUT_BYTES);  // [BM] mean
+    float* const rsl = msl + BM;                        // [BM] rstd
+    for (int r = tid; r < BM; r += NT) {
+      const int m = m0 + r;
+      float mu = 0.0f, rs = 0.0f;
+      if (m < M) {
+        const double s1 = __hip_atomic_load(&p.row_sums[2 * (size_t)m], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        const double s2 = __hip_atomic_load(&p.row_sums[2 * (size_t)m + 1], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        const double mean = p.layernorm ? s1 / N : 0.0;
+        double var = s2 / N - mean * mean;
+        if (var < 0.0) var = 0.0;
+        const double rstd = ok ? 1.0 / sqrt(var + (double)p.eps) : __builtin_nan("");
+        if (tn == 0) {
+          p.stats[2 * (size_t)m] = mean;
+          p.stats[2 * (size_t)m + 1] = rstd;
+        }
+        mu = (float)mean;
+        rs = (float)rstd;
+      }
+      msl[r] = mu;
+      rsl[r] = rs;
+    }
+    __syncthreads();
+    static_for<FM>([&](auto fm_c) {
+      constexpr int fm = decltype(fm_c)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      const int rl = wrow0 + fm * kMfma + lrow;
+      const float mu = msl[rl], rs = rsl[rl];
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int cl = wcol0 + fn * kMfma + 4 * lgrp;
+        float y[kAccN];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const int c_loc = cl + kColStride * g;
+          const u32x2 rw = *(const u32x2*)staged4(rl, c_loc);
+          const f32x4 b4 = *(const f32x4*)(bsl + c_loc);
+          const f32x4 g4 = *(const f32x4*)(gsl + c_loc);
+          const f32x4 e4 = *(const f32x4*)(esl + c_loc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint16_t rb = (uint16_t)(rw[e >> 1] >> (16 * (e & 1)));
+            const float yv = acc[fm][fn][4 * g + e] + b4[e] + to_f32(__builtin_bit_cast(T, rb));
+            float v = (yv - mu) * rs * g4[e];
+            if (has_beta) v += e4[e];
+            y[4 * g + e] = v;
+          }
+        }
+        stage(rl, cl, y);
+      }
+    });
   } else if (epi == EPI_BIAS_RES_SUMS) {
     // y = acc + bias[n] + residual[m, n].  The residual tile is first copied
     // into the staging buffer with row-contiguous 16-byte loads (zeros
@@ -1352,6 +1519,20 @@ hipError_t launch_tile(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WM, WN, NS, BT, SCHED, MT>), dim3(blocks), dim3(WM * WN * 64),
                      0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, bool BT>
+hipError_t blocks_per_cu_by_tile(int tile, int* n) {
+  switch (tile) {
+#define GEMMEPI_CASE(id, bm, bn, bk, wm, wn, ns, pp, mt)                                     \
+  case id:                                                                                 \
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(                                   \
+        n, gemm_kernel<T, bm, bn, bk, wm, wn, ns, BT, pp, mt>, wm * wn * 64, 0);
+    GEMMEPI_TILES(GEMMEPI_CASE)
+#undef GEMMEPI_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 template <typename T, bool BT>

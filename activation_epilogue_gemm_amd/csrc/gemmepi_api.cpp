@@ -12,6 +12,7 @@
 // tile table lookup, done on the host without touching the GPU.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -32,6 +33,12 @@ namespace gemmepi {
    #bm "x" #bn "x" #bk "_w" #wm "x" #wn "_s" #ns "_p" #sched "_m" #mt},
 const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
 #undef GEMMEPI_TILE_ENTRY
+// the single-pass norm's row counters (gemmepi_norm_stats_bytes) assume
+// tiles of at least 64 rows
+#define GEMMEPI_TILE_ROWS(id, bm, bn, bk, wm, wn, ns, sched, mt) \
+  static_assert(bm >= 64, "norm row counters: tile rows");
+GEMMEPI_TILES(GEMMEPI_TILE_ROWS)
+#undef GEMMEPI_TILE_ROWS
 
 // Relative throughput of one CU on a full tile of each configuration, and
 // how many of its workgroups fit on one CU (LDS and registers).  Used only
@@ -59,6 +66,28 @@ hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hip
   if (dtype == DT_F16)
     return b_trans ? launch_gemm_f16_bt(tile, a, s) : launch_gemm_f16_bn(tile, a, s);
   return b_trans ? launch_gemm_bf16_bt(tile, a, s) : launch_gemm_bf16_bn(tile, a, s);
+}
+
+// (cached: the kernels are built for one architecture)
+hipError_t gemm_blocks_per_cu(int dtype, bool b_trans, int tile, int* n) {
+  static std::atomic<int> cache[2][2][kNumTiles];
+  if (tile < 0 || tile >= kNumTiles || (dtype != DT_F16 && dtype != DT_BF16))
+    return hipErrorInvalidValue;
+  std::atomic<int>& c = cache[dtype][b_trans ? 1 : 0][tile];
+  int v = c.load(std::memory_order_relaxed);
+  if (v > 0) {
+    *n = v;
+    return hipSuccess;
+  }
+  hipError_t e;
+  if (dtype == DT_F16)
+    e = b_trans ? blocks_per_cu_f16_bt(tile, &v) : blocks_per_cu_f16_bn(tile, &v);
+  else
+    e = b_trans ? blocks_per_cu_bf16_bt(tile, &v) : blocks_per_cu_bf16_bn(tile, &v);
+  if (e != hipSuccess) return e;
+  if (v > 0) c.store(v, std::memory_order_relaxed);
+  *n = v;
+  return hipSuccess;
 }
 
 }  // namespace gemmepi
@@ -167,7 +196,7 @@ gemmepi_status_t fail(gemmepi_status_t s, const char* fmt, ...) {
 constexpr uint32_t kAllFlags = GEMMEPI_FLAG_B_TRANS | GEMMEPI_FLAG_BIAS_PER_COL |
                                GEMMEPI_FLAG_UNFUSED | GEMMEPI_FLAG_VALIDATE |
                                GEMMEPI_FLAG_NO_DECODE | GEMMEPI_FLAG_SPLIT_K |
-                               GEMMEPI_FLAG_STAGE_B;
+                               GEMMEPI_FLAG_STAGE_B | GEMMEPI_FLAG_NORM_TWO_PASS;
 constexpr int kMaxSplits = 64;
 // Split-K cost model, fitted to a measured (tile, splits) sweep on one
 // MI355X: a split unit pays for its partial-tile round trip about as much
@@ -315,6 +344,24 @@ gemmepi_status_t check_device() {
                   prop.gcnArchName);
   }
   if (ok_dev[dev] < 0) return fail(GEMMEPI_ERR_HIP, "device %d is not gfx950", dev);
+  return GEMMEPI_OK;
+}
+
+// Compute units of the current device (cached per device).
+gemmepi_status_t device_cus(int* cus) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(GEMMEPI_ERR_DEVICE, "device index %d out of range", dev);
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0)
+      return fail(GEMMEPI_ERR_HIP, "compute unit count: %s", hipGetErrorString(e));
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
   return GEMMEPI_OK;
 }
 
@@ -757,23 +804,47 @@ gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const 
 
   hipStream_t s = (hipStream_t)stream;
   const int M = (int)p.M, N = (int)p.N;
+  const bool bt = (p.flags & GEMMEPI_FLAG_B_TRANS) != 0;
   hipError_t e = hipSuccess;
   (void)hipGetLastError();
   GemmArgs g = gemm_args(p, A, B, out);
+  // Single pass when the whole grid is resident at once (every workgroup of
+  // a tile row must reach the row wait); otherwise the GEMM writes y and a
+  // second kernel normalises it.
+  bool one_pass = false;
+  if (!unfused && !(p.flags & GEMMEPI_FLAG_NORM_TWO_PASS)) {
+    int per_cu = 0, cus = 0;
+    if ((st = device_cus(&cus)) != GEMMEPI_OK) return st;
+    e = gemm_blocks_per_cu(p.dtype, bt, p.tile, &per_cu);
+    if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "occupancy query: %s", hipGetErrorString(e));
+    one_pass = (int64_t)p.tiles_m * p.tiles_n <= (int64_t)per_cu * cus;
+  }
   if (!unfused) {
-    // the GEMM adds fp64 partial row sums into stats: zero them first
-    e = launch_fill_f32((float*)stats, (int64_t)M * 4, 0.0f, s);
+    // the sums (and the row counters) start at zero; the whole buffer is
+    // cleared, so row_sync[0] reads 0 after a two-pass execution
+    e = launch_fill_f32((float*)stats, (int64_t)(gemmepi_norm_stats_bytes(M) / 4), 0.0f, s);
     if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "stats fill: %s", hipGetErrorString(e));
     g.bias = bias;
     g.residual = residual;
     g.stats = (double*)stats;
-    g.epi = EPI_BIAS_RES_SUMS;
     g.bias_per_col = 1;
+    if (one_pass) {
+      g.epi = EPI_BIAS_RES_NORM;
+      g.gamma = gamma;
+      g.beta = beta;
+      g.eps = eps;
+      g.layernorm = layernorm ? 1 : 0;
+      g.row_sums = (double*)stats + 2 * (size_t)M;
+      g.row_sync = (uint32_t*)((double*)stats + 4 * (size_t)M);
+    } else {
+      g.epi = EPI_BIAS_RES_SUMS;
+    }
   } else {
     g.epi = EPI_DEFAULT;
   }
-  e = launch_gemm(p.dtype, (p.flags & GEMMEPI_FLAG_B_TRANS) != 0, p.tile, g, s);
+  e = launch_gemm(p.dtype, bt, p.tile, g, s);
   if (e != hipSuccess) return fail(GEMMEPI_ERR_HIP, "gemm kernel: %s", hipGetErrorString(e));
+  if (one_pass) return GEMMEPI_OK;
   if (unfused) {
     if (bias) e = launch_bias_add(p.dtype, out, bias, M, N, N, 1, s);
     if (e == hipSuccess && residual) e = launch_residual_add(p.dtype, out, residual, M, N, N, s);
@@ -786,7 +857,14 @@ gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const 
   return GEMMEPI_OK;
 }
 
-size_t gemmepi_norm_stats_bytes(int64_t M) { return M < 1 ? 0 : (size_t)M * 16; }
+// (mean, rstd) [M][2] fp64, the row sums [M][2] fp64 of the single pass, then
+// row_sync: a status word and one arrival count per tile row (every tile has
+// at least 64 rows), rounded up to 16 bytes
+size_t gemmepi_norm_stats_bytes(int64_t M) {
+  if (M < 1) return 0;
+  const size_t sync_words = 1 + (size_t)((M + 63) / 64);
+  return ((size_t)M * 32 + sync_words * 4 + 15) & ~(size_t)15;
+}
 
 gemmepi_status_t gemmepi_plan_destroy(gemmepi_plan_t plan) {
   if (!plan) return fail(GEMMEPI_ERR_INVALID_VALUE, "plan_destroy: null plan");

@@ -22,7 +22,13 @@ enum Epi : int {
   // GEMM-kernel epilogue of both norms (not a public value): y = acc + bias
   // + residual rounded to out, fp64 partial row sums of y and y^2 added into
   // stats
-  EPI_BIAS_RES_SUMS = 16
+  EPI_BIAS_RES_SUMS = 16,
+  // GEMM-kernel epilogue of the single-pass norm (not a public value): y =
+  // acc + bias + residual kept in fp32 registers; the workgroups of a tile
+  // row add fp64 partial row sums of y and y^2 into row_sums, count their
+  // arrival in row_sync and wait for the whole row; each then normalises its
+  // own tile and writes it once
+  EPI_BIAS_RES_NORM = 17
 };
 
 enum DType : int { DT_F16 = 0, DT_BF16 = 1 };
@@ -38,7 +44,16 @@ struct GemmArgs {
   void* out;         // [M, ldo]
   float* bgrad;      // [N] fp32, pre-zeroed (DRELU_BGRAD)
   const void* residual;  // [M, ldo] in the output dtype or null (BIAS_RES_SUMS)
-  double* stats;     // [M][2] fp64 row sums of y, y^2, pre-zeroed (BIAS_RES_SUMS)
+  double* stats;     // [M][2] fp64: row sums of y, y^2, pre-zeroed (BIAS_RES_SUMS);
+                     // (mean, rstd) written by the tile-column-0 workgroups (BIAS_RES_NORM)
+  // single-pass norm (BIAS_RES_NORM)
+  const void* gamma;   // [N] in the input dtype
+  const void* beta;    // [N] in the input dtype, or null
+  float eps;
+  int layernorm;       // 1: LayerNorm, 0: RMSNorm
+  double* row_sums;    // [M][2] fp64 sums of y and y^2, pre-zeroed
+  uint32_t* row_sync;  // [0]: status (bit 0 ran, bit 1 a wait gave up); [1 + tm]: arrivals
+                       // of tile row tm; pre-zeroed
   int M, N, K;
   int lda, ldb, ldo;
   int aux_ld;        // words per mask row
@@ -87,6 +102,9 @@ extern const TileCfg kTiles[kNumTiles];
 // Launchers (defined in the per-dtype/per-layout instantiation files).
 // Return hipSuccess or the launch error.
 hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s);
+// Workgroups of the tile's GEMM kernel that one CU holds at once
+// (hipOccupancyMaxActiveBlocksPerMultiprocessor).
+hipError_t gemm_blocks_per_cu(int dtype, bool b_trans, int tile, int* n);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
 // Rows of W per workgroup of the row-streaming decode kernel for M tokens,
 // or 0 when the MFMA decode kernel (16 rows per workgroup) runs.
@@ -128,5 +146,9 @@ hipError_t launch_gemm_f16_bn(int tile, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_f16_bt(int tile, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_bn(int tile, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_bf16_bt(int tile, const GemmArgs& a, hipStream_t s);
+hipError_t blocks_per_cu_f16_bn(int tile, int* n);
+hipError_t blocks_per_cu_f16_bt(int tile, int* n);
+hipError_t blocks_per_cu_bf16_bn(int tile, int* n);
+hipError_t blocks_per_cu_bf16_bt(int tile, int* n);
 
 }  // namespace gemmepi

@@ -212,18 +212,21 @@ class NormWorkload:
         self.A, self.B = up(c.A), up(c.B)
         self.bias, self.res, self.gamma, self.beta = up(c.bias), up(c.residual), up(c.gamma), up(c.beta)
         self.out = torch.empty(c.M, c.N, dtype=torch_dtype(c.dtype), device="cuda")
-        self.stats = torch.empty(c.M, 2, dtype=torch.float64, device="cuda")
+        self.stats = ge.norm_stats_buffer(c.M)
         f = ge.FLAG_B_TRANS if c.b_trans else 0
         epi = "BIAS_RES_" + c.norm
         self.fused = ge.plan(c.M, c.N, c.K, c.dtype, epi, f)
         self.unfused = ge.plan(c.M, c.N, c.K, c.dtype, epi, f | ge.FLAG_UNFUSED)
+        # the two-kernel form (GEMM writes y, a second kernel normalises), for
+        # comparison with the single pass that `fused` runs
+        self.two_pass = ge.plan(c.M, c.N, c.K, c.dtype, epi, f | ge.FLAG_NORM_TWO_PASS)
         self.flops = 2.0 * c.M * c.N * c.K
         # operands, residual, gamma/beta/bias, output and stats moved once
         self.bytes = 2 * (c.M * c.K + c.N * c.K + 2 * c.M * c.N + 3 * c.N) + 16 * c.M
         self.rotation = None
 
-    def run(self, unfused=False, i=0):
-        p = self.unfused if unfused else self.fused
+    def run(self, unfused=False, i=0, two_pass=False):
+        p = self.unfused if unfused else (self.two_pass if two_pass else self.fused)
         p.execute_norm(self.A, self.B, self.bias, self.res, self.gamma, self.beta, self.case.eps,
                        self.stats, self.out, check=False)
 
@@ -761,6 +764,19 @@ def main():
                  "plan": w.fused.info()}
         if w in extras:
             entry.update({"in_step": False, "gbs_algorithmic": round(w.bytes / f_ms / 1e6, 1)})
+        if isinstance(w, NormWorkload):
+            import statistics
+            w.run(False, 0)
+            torch.cuda.synchronize()
+            single = ge.norm_pass_status(w.stats, w.case.M) == 1
+            for i in range(2):
+                w.run(False, i, two_pass=True)
+            trials = [time_region(lambda i: w.run(False, i, two_pass=True), reps, stream)
+                      for _ in range(TRIALS)]
+            t_ms = statistics.median(trials)
+            entry.update({"two_pass_ms": round(t_ms, 5), "two_pass_min_ms": round(min(trials), 5),
+                          "speedup_vs_two_pass": round(t_ms / f_ms, 4),
+                          "single_pass": single})
         if w.name.startswith("c1_"):
             gbs = w.bytes / f_ms / 1e6
             # the practical floor: the fastest launch shape of a plain 128-bit

@@ -122,7 +122,11 @@ enum {
    * device workspace (gemmepi_workspace_bytes) and runs through
    * gemmepi_execute_ws.  No effect with B_TRANS, on the decode kernel and on
    * the norm epilogues. */
-  GEMMEPI_FLAG_STAGE_B = 1u << 6
+  GEMMEPI_FLAG_STAGE_B = 1u << 6,
+  /* gemmepi_execute_norm: always run the two-kernel form (the GEMM writes y,
+   * rounded to the dtype, then a second kernel normalises it in place)
+   * instead of the single pass.  For comparison and testing. */
+  GEMMEPI_FLAG_NORM_TWO_PASS = 1u << 7
 };
 
 /* Opaque, reference-counted handle to a cached plan. */
@@ -326,11 +330,17 @@ gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void
  *   LAYERNORM: mean_m = mean(y[m,:]), rstd_m = 1 / sqrt(var(y[m,:]) + eps)
  *   RMSNORM:   mean_m = 0,            rstd_m = 1 / sqrt(mean(y[m,:]^2) + eps)
  *
- * The GEMM kernel writes y (rounded once to the dtype) into out and adds
- * fp64 partial row sums of y and y^2 into stats; a second kernel then
- * normalises each row of out in place.  With GEMMEPI_FLAG_UNFUSED the GEMM
- * writes A.B, and separate kernels add the bias, add the residual and
- * normalise (statistics from the row itself).
+ * Single pass (the default, when the plan's whole grid of workgroups fits
+ * on the device at once): y stays in the GEMM kernel's fp32 registers and is
+ * never rounded before the norm; the workgroups that share a band of rows
+ * add fp64 partial row sums of y and y^2 into the stats workspace, wait
+ * until the whole band has arrived, then each normalises its own tile and
+ * writes out once.  Otherwise (a larger grid, or GEMMEPI_FLAG_NORM_TWO_PASS)
+ * two kernels: the GEMM writes y (rounded once to the dtype) into out and
+ * adds the row sums, then a second kernel normalises each row of out in
+ * place.  With GEMMEPI_FLAG_UNFUSED the GEMM writes A.B, and separate
+ * kernels add the bias, add the residual and normalise (statistics from
+ * the row itself).
  *
  *   A, B      as gemmepi_execute (B [K,N], or [N,K] with B_TRANS)
  *   bias      dtype [N] (always per column), 2-byte aligned, or NULL (none)
@@ -338,11 +348,17 @@ gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void
  *   gamma     dtype [N], 2-byte aligned; required
  *   beta      dtype [N], 2-byte aligned, or NULL (none); ignored by RMSNORM
  *   eps       > 0, finite
- *   stats     fp64 [M][2], 8-byte aligned, gemmepi_norm_stats_bytes(M)
- *             bytes; workspace during the call, on return row m holds
- *             (mean_m, rstd_m)
- *   out       dtype [M,N], 16-byte aligned; overwritten (holds y between
- *             the two kernels)
+ *   stats     gemmepi_norm_stats_bytes(M) bytes, 8-byte aligned; the
+ *             caller's workspace during the call.  On return its first
+ *             16 M bytes are fp64 [M][2]: row m holds (mean_m, rstd_m).
+ *             A fused execution clears the rest; the 32-bit word at byte
+ *             offset 32 M then reads 1 after a single pass and 0 after two
+ *             kernels (UNFUSED leaves it as it was); if its bit 1 is
+ *             set, a workgroup of the single pass stopped waiting for its
+ *             band of rows (bounded at a few seconds; it cannot happen when
+ *             the grid is resident as required) and wrote NaN rows.
+ *   out       dtype [M,N], 16-byte aligned; overwritten (in the two-kernel
+ *             form it holds y between the two kernels)
  * Errors: INVALID_VALUE (null plan or required pointer, not a norm plan,
  * eps not positive and finite), MISALIGNED, DEVICE (VALIDATE), HIP.
  */
@@ -351,8 +367,9 @@ gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const 
                                       const void* gamma, const void* beta, float eps,
                                       void* stats, void* out, void* stream);
 
-/* Bytes of the stats buffer of gemmepi_execute_norm for M rows (16 M);
- * 0 for M < 1.  The statistics of the MatMul + Norm operator of the ops-nn
+/* Bytes of the stats buffer of gemmepi_execute_norm for M rows: 32 M for
+ * (mean, rstd) and the row sums, plus one 32-bit word per 64 rows and a
+ * status word, rounded up to 16; 0 for M < 1.  The statistics of the MatMul + Norm operator of the ops-nn
  * MatMul fusion article, section "Level 2: structural fusion". */
 size_t gemmepi_norm_stats_bytes(int64_t M);
 

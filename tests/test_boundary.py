@@ -194,7 +194,11 @@ def test_norm_entry_point_validation():
     """execute and execute_norm reject each other's plans, and execute_norm
     checks its pointers and eps before any HIP call."""
     lib = ge.library()
-    assert ge.norm_stats_bytes(1000) == 16000 and ge.norm_stats_bytes(0) == 0
+    # (mean, rstd) and the row sums (32 M bytes), a status word and one
+    # counter per 64 rows, rounded up to 16 bytes
+    assert ge.norm_stats_bytes(1000) == 32000 + 4 * (1 + 16) + 12
+    assert ge.norm_stats_bytes(64) == 2048 + 16 and ge.norm_stats_bytes(0) == 0
+    assert all(ge.norm_stats_bytes(m) % 16 == 0 for m in range(1, 300))
     with ge.plan(64, 64, 64, "f16", "BIAS_RES_LAYERNORM", ge.FLAG_B_TRANS) as p:
         assert "path=gemm" in p.info()          # never the decode kernel
         h = p._h

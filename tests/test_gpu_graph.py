@@ -80,10 +80,13 @@ def test_graph_replays_match_eager(epi, b_trans, tile, splits):
         del g
 
 
+@pytest.mark.parametrize("two_pass", [False, True])
 @pytest.mark.parametrize("norm", ["LAYERNORM", "RMSNORM"])
-def test_graph_replays_norm_match_eager(norm):
-    """The norm operator is three launches (statistics fill, GEMM, row norm);
-    captured and replayed with new inputs it must match eager execution."""
+def test_graph_replays_norm_match_eager(norm, two_pass):
+    """The norm operator is two launches in its single pass (workspace fill,
+    GEMM with the row wait) and three in the two-kernel form (fill, GEMM, row
+    norm); captured and replayed with new inputs it must match eager
+    execution, workspace included."""
     import torch
     M, N, K = 264, 320, 136
     cases = [wl.norm_case(M, N, K, "f16", norm, True, 300 + 11 * r, kind="int") for r in range(3)]
@@ -92,14 +95,15 @@ def test_graph_replays_norm_match_eager(norm):
         up = lambda x: upload_bits(x, "f16")  # noqa: E731
         return {"A": up(c.A), "B": up(c.B), "bias": up(c.bias), "res": up(c.residual),
                 "gamma": up(c.gamma), "beta": up(c.beta),
-                "stats": torch.zeros(M, 2, dtype=torch.float64, device="cuda"),
+                "stats": ge.norm_stats_buffer(M),
                 "out": torch.empty(M, N, dtype=torch.float16, device="cuda")}
 
     def run(p, b):
         p.execute_norm(b["A"], b["B"], b["bias"], b["res"], b["gamma"], b["beta"], 0.25,
                        b["stats"], b["out"])
 
-    with ge.plan(M, N, K, "f16", "BIAS_RES_" + norm, ge.FLAG_B_TRANS) as p:
+    flags = ge.FLAG_B_TRANS | (ge.FLAG_NORM_TWO_PASS if two_pass else 0)
+    with ge.plan(M, N, K, "f16", "BIAS_RES_" + norm, flags) as p:
         cap = bufs(cases[0])
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -123,4 +127,5 @@ def test_graph_replays_norm_match_eager(norm):
             torch.cuda.synchronize()
             assert np.array_equal(download_bits(cap["out"]), download_bits(new["out"])), f"replay {r}: out"
             assert torch.equal(cap["stats"], new["stats"]), f"replay {r}: stats"
+            assert ge.norm_pass_status(cap["stats"], M) == (0 if two_pass else 1)
         del g

@@ -313,8 +313,10 @@ def test_split_flag_chooses_only_for_wave_quantised_shapes():
             return p.info(), p.workspace_bytes()
     i, ws = info(512, 4096, 11008, True)       # 512-token FFN down-projection
     assert "splits=" in i and ws > 0, i
-    for M, N, K, bt in ((65536, 8192, 16384, False), (2048, 4096, 11008, True),
-                        (4096, 4096, 4096, True)):
+    # 2048-token FFN down-projection: 128 tiles of 256 x 256, split twice
+    i, ws = info(2048, 4096, 11008, True)
+    assert f"tile={ge.tile_name(8)}" in i and "splits=2" in i and ws > 0, i
+    for M, N, K, bt in ((65536, 8192, 16384, False), (4096, 4096, 4096, True)):
         i, ws = info(M, N, K, bt)
         assert "splits=" not in i and ws == 0, i
 

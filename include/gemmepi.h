@@ -42,7 +42,10 @@
 extern "C" {
 #endif
 
-#define GEMMEPI_VERSION 100 /* 1.0.0 */
+/* 1.1.0: the stats buffer of gemmepi_execute_norm grew to
+ * gemmepi_norm_stats_bytes(M) (32 M bytes and row counters, was 16 M) for the
+ * single-pass norm; GEMMEPI_FLAG_NORM_TWO_PASS added. */
+#define GEMMEPI_VERSION 110
 
 typedef enum {
   GEMMEPI_OK = 0,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     lib = ge.library()
     missing = [n for n in declared_functions() if not hasattr(lib, n)]
     assert not missing, missing
-    assert ge.version() == 100
+    assert ge.version() == 110
 
 
 def _plan_status(M, N, K, dtype=0, epi=1, flags=0, tile=-1):

@@ -992,6 +992,48 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // all loads of a slot would spill the accumulators)
     constexpr int FNG = kAccN == 16 ? (FN > 2 ? 1 : FN) : (FN > 4 ? 4 : FN);  // blocks per step
     static_assert(FN % FNG == 0, "split-K load steps");
+    // Two splits on the 32 x 32 MFMA tiles (the small tiles, whose
+    // accumulators leave registers to spare): only the other split's slot is
+    // read; this split's partial is still in its accumulators.  The general
+    // path below forms (0 + slot 0) + slot 1; here split 0 forms
+    // (0 + acc) + slot 1 and split 1 forms (0 + slot 0) + acc, the same bits
+    // (a + b == b + a exactly), so the result still does not depend on which
+    // split arrived last.  The loads of each step are issued one step
+    // ahead.  (On the 256-wide tiles a second path here costs spills.)
+    if (kAccN == 16 && p.splits == 2) {
+      const float* src = slots + (size_t)(1 - split) * (QE * NT);
+      constexpr bool kAhead = true;
+      constexpr int NF = FN / FNG, NSTEP = FM * NF;
+      float v[kAhead ? 2 : 1][FNG][kAccN];
+      auto issue = [&](auto st_c) {
+        constexpr int st = decltype(st_c)::value;
+        constexpr int fm = st / NF, f0 = (st % NF) * FNG, b = kAhead ? (st & 1) : 0;
+#pragma unroll
+        for (int j = 0; j < FNG; ++j)
+#pragma unroll
+          for (int r = 0; r < kAccN; ++r)
+            v[b][j][r] = __hip_atomic_load(src + ((fm * FN + f0 + j) * kAccN + r) * NT + tid,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      if constexpr (kAhead) issue(std::integral_constant<int, 0>{});
+      const bool first = split == 0;
+      static_for<NSTEP>([&](auto st_c) {
+        constexpr int st = decltype(st_c)::value;
+        constexpr int fm = st / NF, f0 = (st % NF) * FNG, b = kAhead ? (st & 1) : 0;
+        if constexpr (!kAhead)
+          issue(st_c);
+        else if constexpr (st + 1 < NSTEP)
+          issue(std::integral_constant<int, st + 1>{});
+#pragma unroll
+        for (int j = 0; j < FNG; ++j)
+#pragma unroll
+          for (int r = 0; r < kAccN; ++r) {
+            const float a = acc[fm][f0 + j][r], c = v[b][j][r];
+            acc[fm][f0 + j][r] = (0.0f + (first ? a : c)) + (first ? c : a);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else
     for (int s = 0; s < p.splits; ++s) {
       const float* src = slots + (size_t)s * (QE * NT);
       static_for<FM>([&](auto fm_c) {

@@ -64,10 +64,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Out-of-range voffset: larger than the descriptor's record count, so the
 // buffer load returns zeros.
 constexpr uint32_t kOOB = 0x80000000u;
-// Polls of the single-pass norm's row wait before a workgroup gives up
-// (each poll: one device-coherent load and a ~128-cycle sleep; the bound is
-// in the seconds, where a normal wait lasts microseconds).
-constexpr uint32_t kNormWaitPolls = 1u << 21;
 constexpr int kNumRecords = 0x7FFFFFFF;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
@@ -1275,7 +1271,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       for (uint32_t polls = 0;
            __hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)p.tiles_n;
            ++polls) {
-        if (polls >= kNormWaitPolls) {
+        if (polls >= p.norm_wait_polls) {
           ok = 0u;
           break;
         }

@@ -348,6 +348,18 @@ gemmepi_status_t check_device() {
   return GEMMEPI_OK;
 }
 
+// Poll bound of the single-pass norm's row wait: kNormWaitPolls, or
+// GEMMEPI_NORM_WAIT_POLLS (read at every call) to force the give-up path in
+// a test (0: a workgroup that is not the last of its band gives up at once).
+uint32_t norm_wait_polls() {
+  const char* e = getenv("GEMMEPI_NORM_WAIT_POLLS");
+  if (!e || !*e) return kNormWaitPolls;
+  char* end = nullptr;
+  const unsigned long v = strtoul(e, &end, 10);
+  if (!end || *end != '\0' || v > kNormWaitPolls) return kNormWaitPolls;
+  return (uint32_t)v;
+}
+
 // Compute units of the current device (cached per device).
 gemmepi_status_t device_cus(int* cus) {
   static std::atomic<int> cache[64];
@@ -837,6 +849,7 @@ gemmepi_status_t gemmepi_execute_norm(gemmepi_plan_t plan, const void* A, const 
       g.layernorm = layernorm ? 1 : 0;
       g.row_sums = (double*)stats + 2 * (size_t)M;
       g.row_sync = (uint32_t*)((double*)stats + 4 * (size_t)M);
+      g.norm_wait_polls = norm_wait_polls();
     } else {
       g.epi = EPI_BIAS_RES_SUMS;
     }

@@ -54,6 +54,7 @@ struct GemmArgs {
   double* row_sums;    // [M][2] fp64 sums of y and y^2, pre-zeroed
   uint32_t* row_sync;  // [0]: status (bit 0 ran, bit 1 a wait gave up); [1 + tm]: arrivals
                        // of tile row tm; pre-zeroed
+  uint32_t norm_wait_polls;  // polls of the row wait before a workgroup gives up
   int M, N, K;
   int lda, ldb, ldo;
   int aux_ld;        // words per mask row
@@ -102,6 +103,11 @@ extern const TileCfg kTiles[kNumTiles];
 // Launchers (defined in the per-dtype/per-layout instantiation files).
 // Return hipSuccess or the launch error.
 hipError_t launch_gemm(int dtype, bool b_trans, int tile, const GemmArgs& a, hipStream_t s);
+// Polls of the single-pass norm's row wait before a workgroup gives up
+// (each poll: one device-coherent load and a ~128-cycle sleep; the bound is
+// in the seconds, where a normal wait lasts microseconds).
+constexpr uint32_t kNormWaitPolls = 1u << 21;
+
 // Workgroups of the tile's GEMM kernel that one CU holds at once
 // (hipOccupancyMaxActiveBlocksPerMultiprocessor).
 hipError_t gemm_blocks_per_cu(int dtype, bool b_trans, int tile, int* n);

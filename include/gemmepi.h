@@ -359,7 +359,10 @@ gemmepi_status_t gemmepi_autotune(gemmepi_plan_t plan, const void* A, const void
  *             kernels (UNFUSED leaves it as it was); if its bit 1 is
  *             set, a workgroup of the single pass stopped waiting for its
  *             band of rows (bounded at a few seconds; it cannot happen when
- *             the grid is resident as required) and wrote NaN rows.
+ *             the grid is resident as required) and wrote NaN rows.  The
+ *             environment variable GEMMEPI_NORM_WAIT_POLLS (0 to 2^21 polls,
+ *             read at every call) lowers that bound, to test this path.
+ *             Calls that share one stats buffer must not overlap.
  *   out       dtype [M,N], 16-byte aligned; overwritten (in the two-kernel
  *             form it holds y between the two kernels)
  * Errors: INVALID_VALUE (null plan or required pointer, not a norm plan,

@@ -286,7 +286,7 @@ def check_bgrad(case, got: np.ndarray, ref, label: str = "", unfused: bool = Fal
 # ---------------------------------------------------------------- GEMM + residual + norm
 
 
-def run_norm(c, flags: int = 0, tile: int = -1, eps=None):
+def run_norm(c, flags: int = 0, tile: int = -1, eps=None, allow_gave_up: bool = False):
     """Upload a NormCase, execute it through gemmepi_execute_norm and return
     (out bits [M, N], (mean, rstd) fp64 [M, 2], status word: 1 single pass,
     0 two kernels)."""
@@ -304,7 +304,7 @@ def run_norm(c, flags: int = 0, tile: int = -1, eps=None):
         p.execute_norm(A, B, bias, res, gamma, beta, c.eps if eps is None else eps, stats, out)
         torch.cuda.synchronize()
     status = ge.norm_pass_status(stats, c.M)
-    assert status in (0, 1), f"{c.name}: norm status word {status:#x} (a row wait gave up)"
+    assert status in (0, 1) or allow_gave_up, f"{c.name}: norm status word {status:#x} (a row wait gave up)"
     return download_bits(out), ge.norm_mean_rstd(stats, c.M).cpu().numpy(), status
 
 

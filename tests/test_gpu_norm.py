@@ -99,6 +99,26 @@ def test_norm_grid_larger_than_the_chip_takes_two_kernels():
         _run_check(c, rows, _ref(c, rows), f"M{M}", tile=7, expect_status=expect)
 
 
+def test_norm_wait_gives_up_when_forced(monkeypatch):
+    """The single pass's row wait is bounded.  With the bound forced to zero
+    polls (GEMMEPI_NORM_WAIT_POLLS=0) a workgroup that does not see its whole
+    band arrived at its first poll gives up: the call still completes, bit 1
+    of the status word is set and that workgroup's rows are NaN (a loud
+    result, never a hang).  Without the override the next call is correct."""
+    c = wl.norm_case(512, 1024, 64, "f16", "LAYERNORM", True, 41)
+    monkeypatch.setenv("GEMMEPI_NORM_WAIT_POLLS", "0")
+    gave_up = 0
+    for _ in range(3):
+        out, _, status = run_norm(c, allow_gave_up=True)
+        assert status & 1, f"status {status:#x}: not the single pass"
+        if status & 2:
+            gave_up += 1
+            assert np.isnan(O.decode(out, c.dtype)).any(), "a wait gave up but no row is NaN"
+    assert gave_up > 0, "no workgroup gave up with a zero poll bound"
+    monkeypatch.delenv("GEMMEPI_NORM_WAIT_POLLS")
+    _run_check(c, np.arange(c.M), _ref(c), "after forced give-up", expect_status=1)
+
+
 @pytest.mark.parametrize("norm", ["LAYERNORM", "RMSNORM"])
 def test_norm_ffn_down_full_size(norm):
     """The 2048-token FFN down-projection shape (M 2048, N 4096, K 11008):

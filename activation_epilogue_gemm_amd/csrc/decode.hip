@@ -210,6 +210,7 @@ __device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float c, __bf16) {
 
 template <typename T, int R, int TB>
 __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArgs p) {
+  static_assert(R * TB <= 64, "one epilogue lane of wave 0 per output");
   __shared__ float red[kDecodeWaves][R * TB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -281,27 +282,27 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
 // M = 1, 7.21 against 8.78 at M = 2, 7.96 against 8.78 at M = 3 and 8.18
 // against 8.81 at M = 4, but 13.1-13.9 against 9.1-9.2 at M = 5..8 (each
 // workgroup re-reads every token row, 64 MiB in all at 8 tokens, and the
-// VALU products grow with M); 8 rows per workgroup were slower at every M,
-// 2 rows no faster.
+// VALU products grow with M).  Rows per workgroup, interleaved on one box
+// (M = 1 / 2 / 3 / 4): 4 rows 7.03 / 7.26 / 8.12 / 8.22 us, 8 rows 7.17 /
+// 7.47 / 8.78 / 8.47, 2 rows 7.00 / 7.65 / 8.67 / 9.45.
 #ifndef GEMMEPI_GEMV_ROWS
 #define GEMMEPI_GEMV_ROWS 4
 #endif
 int gemv_rows(int M) { return M <= 4 ? GEMMEPI_GEMV_ROWS : 0; }
 
+// R rows of W per workgroup (GEMMEPI_GEMV_ROWS), TB = 1, 2 or 4 tokens
 template <typename T>
-static void launch_gemv_t(const DecodeArgs& a, int R, hipStream_t s) {
+static void launch_gemv_t(const DecodeArgs& a, hipStream_t s) {
+  constexpr int R = GEMMEPI_GEMV_ROWS;
+  static_assert(R == 1 || R == 2 || R == 4 || R == 8, "rows per workgroup");
   const dim3 block(kDecodeWaves * 64);
   const dim3 grid((a.N + R - 1) / R);
-#define GEMMEPI_GEMV(RR, TT) hipLaunchKernelGGL((gemv_kernel<T, RR, TT>), grid, block, 0, s, a)
-  if (R == 8) {
-    if (a.M <= 1) GEMMEPI_GEMV(8, 1);
-    else GEMMEPI_GEMV(8, 2);
-  } else {
-    if (a.M <= 1) GEMMEPI_GEMV(4, 1);
-    else if (a.M <= 2) GEMMEPI_GEMV(4, 2);
-    else GEMMEPI_GEMV(4, 4);
-  }
-#undef GEMMEPI_GEMV
+  if (a.M <= 1)
+    hipLaunchKernelGGL((gemv_kernel<T, R, 1>), grid, block, 0, s, a);
+  else if (a.M <= 2)
+    hipLaunchKernelGGL((gemv_kernel<T, R, 2>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemv_kernel<T, R, 4>), grid, block, 0, s, a);
 }
 
 template <typename T>
@@ -321,12 +322,11 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) {
   if (a.M < 1 || a.M > 16) return hipErrorInvalidValue;
-  const int R = gemv_rows(a.M);
-  if (R > 0 && a.K % 8 == 0) {
+  if (gemv_rows(a.M) > 0 && a.K % 8 == 0) {
     if (dtype == DT_F16)
-      launch_gemv_t<_Float16>(a, R, s);
+      launch_gemv_t<_Float16>(a, s);
     else
-      launch_gemv_t<__bf16>(a, R, s);
+      launch_gemv_t<__bf16>(a, s);
   } else if (dtype == DT_F16) {
     launch_decode_t<_Float16>(a, s);
   } else {

@@ -11,12 +11,13 @@
 //   * a workgroup owns 16 consecutive output columns n (16 rows of W) and
 //     splits K over its 8 wavefronts;
 //   * each wave issues all of its 128-bit W loads for a 512-wide k window
-//     (16 steps) before consuming any, so one workgroup keeps its whole
-//     16 x K slice of W in flight;
-//   * the token rows x[t, window] are loaded once per wave, one contiguous
-//     1 KiB load per token, into a swizzled LDS window from which the MFMA
-//     fragments are read (loading them in fragment form would cost one
-//     vector memory instruction per k step even for a single token);
+//     before consuming any, so one workgroup keeps its whole 16 x K slice
+//     of W in flight;
+//   * every load instruction reads whole 512-byte row segments (two rows of
+//     W, or two token rows of x, per instruction), and the MFMA fragments
+//     are read from swizzled LDS copies of the window, one 256-wide half at
+//     a time (loading W or x in fragment form, 16 rows x 64 bytes per
+//     instruction, was 11-20 % slower);
 //   * the products run on v_mfma_f32_16x16x32 with W rows as the 16-row
 //     operand and the (zero-padded) tokens as the 16-column operand, which
 //     keeps the multiply-adds off the VALU entirely;
@@ -50,29 +51,39 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeUnroll = 16;            // 32-wide k steps per W batch
 constexpr int kDecodeWin = 32 * kDecodeUnroll;  // k window of one batch (512)
+constexpr int kDecodeHalf = kDecodeWin / 2;     // k of one LDS half (256)
 
-// One wave's copy of the x window: [16 tokens][512 k] fp16 = 16 KiB, with the
-// 16-byte chunk c of token row t stored at chunk c ^ t, so that the MFMA
-// fragment read (16 lanes = 16 token rows at the same logical chunk) and the
-// row writes (64 lanes = 64 chunks of one row) are both bank-conflict-free.
-__device__ __forceinline__ uint32_t xwin_off(int t, int chunk) {
-  return (uint32_t)(t * (kDecodeWin * 2) + ((chunk ^ t) << 4));
+// One wave's LDS copy of a 256-wide half window, [rows][256 k] fp16 (512
+// bytes per row: 16 rows of W, or the token rows of x), with the 16-byte
+// chunk c (0..31) of row r stored at chunk c ^ (r & 15).  The MFMA fragment
+// read (16 lanes = 16 rows at the same logical chunk) then touches 16
+// distinct 16-byte bank groups of the 256-byte bank line, and the row
+// writes (32 lanes = 32 chunks of one row) stay conflict-free.
+__device__ __forceinline__ uint32_t half_off(int r, int chunk) {
+  return (uint32_t)(r * (kDecodeHalf * 2) + ((chunk ^ (r & 15)) << 4));
 }
 
-// TB: token bucket (1, 2, 4, 8 or 16) >= M, so the x loads unroll.
+// TB: token bucket (8 or 16) >= M, so the x loads unroll.  (One to four
+// tokens take the row-streaming kernel below.)
 template <typename T, int TB>
 __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeArgs p) {
+  static_assert(TB == 8 || TB == 16, "token bucket");
   using V8 = typename Frag<T>::type;
-  constexpr int kWPolicy = TB >= 8 ? GEMMEPI_DECODE_W_POLICY : 0;
+  constexpr int kWPolicy = GEMMEPI_DECODE_W_POLICY;
+  constexpr int XI = TB / 2;                  // x load instructions per half (2 tokens each)
+  constexpr int WI = 8;                       // W load instructions per half (2 rows each)
   __shared__ f32x4 red[kDecodeWaves][64];
-  __shared__ __attribute__((aligned(16))) uint8_t xwin[kDecodeWaves][TB * kDecodeWin * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t wtile[kDecodeWaves][16 * kDecodeHalf * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t xtile[kDecodeWaves][TB * kDecodeHalf * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
-  const int r16 = lane & 15;        // W row within the block / token index
+  const int r16 = lane & 15;        // fragment row: W row within the block / token index
   const int kg = lane >> 4;         // k group of this lane within a 32-wide step
+  const int rh = lane >> 5;         // row of a load instruction's pair (0 or 1)
+  const int lc = lane & 31;         // 16-byte chunk of a load instruction's row
   const int kbeg = wave * p.k_per_wave;
   const int kend = min(p.K, kbeg + p.k_per_wave);
   const int Mt = p.M;
@@ -94,38 +105,51 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
 
   const __amdgpu_buffer_rsrc_t rW = make_rsrc((const uint8_t*)p.W + (size_t)n0 * p.ldw * 2);
   const __amdgpu_buffer_rsrc_t rX = make_rsrc(p.x);
-  const bool w_ok = n0 + r16 < p.N;
-  const uint32_t w_row = (uint32_t)(r16 * p.ldw) * 2u;
-  uint8_t* xw = xwin[wave];
+  uint8_t* const wt = wtile[wave];
+  uint8_t* const xt = xtile[wave];
 
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int k = kbeg; k < kend; k += kDecodeWin) {
-    // x first (TB contiguous 1 KiB loads), then the whole W window (16
-    // steps: lane row r16, 8 k values of step u at k + 32 u + 8 kg)
-    u32x4 xl[TB];
+    // All loads of the window, in the order they are consumed: per half,
+    // the token rows (instruction i: tokens 2i and 2i + 1), then the W rows
+    // (instruction j: rows 2j and 2j + 1); lane (rh, lc) reads the 8 k of
+    // chunk lc of its row.
+    u32x4 xl[2][XI], wl[2][WI];
 #pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      const int kk = k + lane * 8;
-      xl[t] = buffer_load16(rX, (t < Mt && kk < kend) ? (uint32_t)(t * p.ldx + kk) * 2u : kOOB);
-    }
-    u32x4 wv[kDecodeUnroll];
+    for (int h = 0; h < 2; ++h) {
+      const int kk = k + h * kDecodeHalf + lc * 8;
+      const bool k_ok = kk < kend;
 #pragma unroll
-    for (int u = 0; u < kDecodeUnroll; ++u) {
-      const int kk = k + u * 32 + kg * 8;
-      wv[u] = __builtin_amdgcn_raw_buffer_load_b128(
-          rW, (kk < kend && w_ok) ? w_row + (uint32_t)kk * 2u : kOOB, 0, kWPolicy);
-    }
+      for (int i = 0; i < XI; ++i) {
+        const int t = 2 * i + rh;
+        xl[h][i] = buffer_load16(rX, (k_ok && t < Mt) ? (uint32_t)(t * p.ldx + kk) * 2u : kOOB);
+      }
 #pragma unroll
-    for (int t = 0; t < TB; ++t) *(u32x4*)(xw + xwin_off(t, lane)) = xl[t];
-    u32x4 xf[kDecodeUnroll];
-#pragma unroll
-    for (int u = 0; u < kDecodeUnroll; ++u) {
-      xf[u] = u32x4{0u, 0u, 0u, 0u};
-      if (r16 < TB) xf[u] = *(const u32x4*)(xw + xwin_off(r16, u * 4 + kg));
+      for (int j = 0; j < WI; ++j) {
+        const int r = 2 * j + rh;
+        wl[h][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            rW, (k_ok && n0 + r < p.N) ? (uint32_t)(r * p.ldw + kk) * 2u : kOOB, 0, kWPolicy);
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kDecodeUnroll; ++u)
-      acc = mfma16(__builtin_bit_cast(V8, wv[u]), __builtin_bit_cast(V8, xf[u]), acc);
+    for (int h = 0; h < 2; ++h) {
+      // the half's rows into this wave's LDS tiles (the previous half's
+      // fragment reads were issued before these writes and LDS keeps a
+      // wave's operations in order)
+#pragma unroll
+      for (int i = 0; i < XI; ++i) *(u32x4*)(xt + half_off(2 * i + rh, lc)) = xl[h][i];
+#pragma unroll
+      for (int j = 0; j < WI; ++j) *(u32x4*)(wt + half_off(2 * j + rh, lc)) = wl[h][j];
+      // 8 MFMA steps of 32 k: W rows as the 16-row operand, the tokens
+      // (rows past TB read as zero) as the 16-column operand
+#pragma unroll
+      for (int u = 0; u < kDecodeUnroll / 2; ++u) {
+        const u32x4 wf = *(const u32x4*)(wt + half_off(r16, 4 * u + kg));
+        u32x4 xf = u32x4{0u, 0u, 0u, 0u};
+        if (r16 < TB) xf = *(const u32x4*)(xt + half_off(r16, 4 * u + kg));
+        acc = mfma16(__builtin_bit_cast(V8, wf), __builtin_bit_cast(V8, xf), acc);
+      }
+    }
   }
 
   red[wave][lane] = acc;
@@ -308,13 +332,7 @@ static void launch_gemv_t(const DecodeArgs& a, hipStream_t s) {
 template <typename T>
 static void launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((a.N + 15) / 16), block(kDecodeWaves * 64);
-  if (a.M <= 1)
-    hipLaunchKernelGGL((decode_kernel<T, 1>), grid, block, 0, s, a);
-  else if (a.M <= 2)
-    hipLaunchKernelGGL((decode_kernel<T, 2>), grid, block, 0, s, a);
-  else if (a.M <= 4)
-    hipLaunchKernelGGL((decode_kernel<T, 4>), grid, block, 0, s, a);
-  else if (a.M <= 8)
+  if (a.M <= 8)
     hipLaunchKernelGGL((decode_kernel<T, 8>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((decode_kernel<T, 16>), grid, block, 0, s, a);

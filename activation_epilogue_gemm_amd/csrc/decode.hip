@@ -63,11 +63,11 @@ __device__ __forceinline__ uint32_t half_off(int r, int chunk) {
   return (uint32_t)(r * (kDecodeHalf * 2) + ((chunk ^ (r & 15)) << 4));
 }
 
-// TB: token bucket (8 or 16) >= M, so the x loads unroll.  (One to four
+// TB: token bucket (4, 8 or 16) >= M, so the x loads unroll.  (One to three
 // tokens take the row-streaming kernel below.)
 template <typename T, int TB>
 __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeArgs p) {
-  static_assert(TB == 8 || TB == 16, "token bucket");
+  static_assert(TB == 4 || TB == 8 || TB == 16, "token bucket");
   using V8 = typename Frag<T>::type;
   constexpr int kWPolicy = GEMMEPI_DECODE_W_POLICY;
   constexpr int XI = TB / 2;                  // x load instructions per half (2 tokens each)
@@ -175,8 +175,8 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) decode_kernel(const DecodeA
   }
 }
 
-// ---- row-streaming decode for one to four tokens -------------------------
-// With M <= 4 the products are too few to need the matrix cores, and the
+// ---- row-streaming decode for one to three tokens ------------------------
+// With M <= 3 the products are too few to need the matrix cores, and the
 // weight stream is best read the way a plain streaming read is fastest: one
 // contiguous 1 KiB per load instruction, and many small workgroups (the
 // stream-read sweep of the benchmark peaks at 32 KiB per workgroup).  A
@@ -301,18 +301,19 @@ __global__ void __launch_bounds__(kDecodeWaves * 64) gemv_kernel(const DecodeArg
 
 // Rows per workgroup of the row-streaming kernel for M tokens; 0: the MFMA
 // decode kernel above.  Measured over the 16 rotated 4096 x 4096 weights
-// against the MFMA kernel, interleaved on one box: 4 rows (bias requested
-// first, DPP reduction, non-temporal weight loads) 6.95 against 8.44 us at
-// M = 1, 7.21 against 8.78 at M = 2, 7.96 against 8.78 at M = 3 and 8.18
-// against 8.81 at M = 4, but 13.1-13.9 against 9.1-9.2 at M = 5..8 (each
-// workgroup re-reads every token row, 64 MiB in all at 8 tokens, and the
-// VALU products grow with M).  Rows per workgroup, interleaved on one box
+// against the MFMA kernel (its row-segment loads; 2- and 4-token buckets for
+// the comparison), interleaved on one box: 6.97 against 7.99 us at M = 1,
+// 7.22 against 8.04 at M = 2, 7.94 against 7.94-8.03 at M = 3, but 8.18
+// against 7.96 at M = 4; from five tokens on the row-streaming kernel falls
+// far behind (13.1-13.9 us at M = 5..8 with the earlier MFMA kernel at
+// 9.1-9.2: each workgroup re-reads every token row, 64 MiB in all at 8
+// tokens, and the VALU products grow with M).  Rows per workgroup, interleaved on one box
 // (M = 1 / 2 / 3 / 4): 4 rows 7.03 / 7.26 / 8.12 / 8.22 us, 8 rows 7.17 /
 // 7.47 / 8.78 / 8.47, 2 rows 7.00 / 7.65 / 8.67 / 9.45.
 #ifndef GEMMEPI_GEMV_ROWS
 #define GEMMEPI_GEMV_ROWS 4
 #endif
-int gemv_rows(int M) { return M <= 4 ? GEMMEPI_GEMV_ROWS : 0; }
+int gemv_rows(int M) { return M <= 3 ? GEMMEPI_GEMV_ROWS : 0; }
 
 // R rows of W per workgroup (GEMMEPI_GEMV_ROWS), TB = 1, 2 or 4 tokens
 template <typename T>
@@ -332,7 +333,9 @@ static void launch_gemv_t(const DecodeArgs& a, hipStream_t s) {
 template <typename T>
 static void launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((a.N + 15) / 16), block(kDecodeWaves * 64);
-  if (a.M <= 8)
+  if (a.M <= 4)
+    hipLaunchKernelGGL((decode_kernel<T, 4>), grid, block, 0, s, a);
+  else if (a.M <= 8)
     hipLaunchKernelGGL((decode_kernel<T, 8>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((decode_kernel<T, 16>), grid, block, 0, s, a);

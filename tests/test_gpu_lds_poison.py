@@ -94,3 +94,24 @@ def test_poisoned_staged_b(poisoned):
     c = wl.random_case(8200, 264, 200, "f16", "RELU_AUX_BIAS", False, False, 9600, kind="int")
     info = exact(c, flags=poisoned.FLAG_STAGE_B)
     assert "stage_b" in info
+
+
+@pytest.mark.parametrize("norm", ["LAYERNORM", "RMSNORM"])
+@pytest.mark.parametrize("tile", range(parity.NUM_TILES))
+def test_poisoned_norm_every_tile(poisoned, tile, norm):
+    """The norm operator through the race-detector build, on every tile:
+    the single pass (residual staged in LDS and read again after the row
+    wait, statistics slices in LDS) and the two-kernel form.  Integer inputs
+    make y and the row sums exact, so both forms must give the same bits; a
+    read of a poisoned or stale LDS slot would give NaN instead."""
+    c = wl.norm_case(272, 320, 96, "f16", norm, True, 9500 + tile, kind="int")
+    o1, s1, st1 = parity.run_norm(c, tile=tile)
+    o2, s2, st2 = parity.run_norm(c, flags=poisoned.FLAG_NORM_TWO_PASS, tile=tile)
+    assert (st1, st2) == (1, 0), f"tile {tile}: status {st1}, {st2}"
+    assert not np.isnan(O.decode(o1, c.dtype)).any(), f"tile {tile}: NaN in the single pass"
+    assert np.array_equal(o1, o2), f"tile {tile}: single pass and two kernels differ"
+    assert np.array_equal(s1, s2), f"tile {tile}: statistics differ"
+    ref = O.gemm_norm(c.A, c.B, c.bias, c.residual, c.gamma, c.beta, c.eps, c.M, c.N, c.K,
+                      c.dtype, c.norm, c.b_trans)
+    parity.check_norm(c, o1, s1, ref, np.arange(c.M), label=f"poison tile {tile}", status=1)
+    say(f"norm {norm} tile {tile} ok")

@@ -302,14 +302,15 @@ void describe(gemmepi_plan_s* p) {
                                "BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM",
                                "GELU_AUX_BIAS", "DGELU_BGRAD"};
   if (p->path == PATH_DECODE) {
-    const int rows = gemv_rows((int)p->M) > 0 ? gemv_rows((int)p->M) : 16;
+    const DecodeKind kind = decode_kind((int)p->M, (int)p->K);
+    const int rows = decode_rows(kind);
+    static const char* kinds[] = {"mfma", "rowstream", "rowwave"};
     snprintf(buf, sizeof(buf),
              "path=decode M=%lld N=%lld K=%lld dtype=%s epi=%s flags=0x%x kernel=%s rows=%d "
-             "grid=%lld waves=8%s",
+             "grid=%lld waves=%d%s",
              (long long)p->M, (long long)p->N, (long long)p->K, p->dtype ? "bf16" : "f16",
-             epis[p->epi], p->flags, gemv_rows((int)p->M) > 0 ? "rowstream" : "mfma", rows,
-             (long long)((p->N + rows - 1) / rows),
-             (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
+             epis[p->epi], p->flags, kinds[kind], rows, (long long)((p->N + rows - 1) / rows),
+             decode_waves(kind), (p->flags & GEMMEPI_FLAG_UNFUSED) ? " unfused" : "");
   } else {
     const TileCfg& c = kTiles[p->tile];
     char split_buf[64] = "";

@@ -112,9 +112,16 @@ constexpr uint32_t kNormWaitPolls = 1u << 21;
 // (hipOccupancyMaxActiveBlocksPerMultiprocessor).
 hipError_t gemm_blocks_per_cu(int dtype, bool b_trans, int tile, int* n);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
-// Rows of W per workgroup of the row-streaming decode kernel for M tokens,
-// or 0 when the MFMA decode kernel (16 rows per workgroup) runs.
-int gemv_rows(int M);
+// The decode kernel for M tokens and reduction length K, and its launch
+// shape (rows of W per workgroup, waves per workgroup).
+enum DecodeKind : int {
+  DECODE_MFMA = 0,       // 16 rows of W per workgroup, MFMA products (4-16 tokens)
+  DECODE_ROWSTREAM = 1,  // 4 rows, 8 waves splitting K, VALU products (1-3 tokens)
+  DECODE_ROWWAVE = 2     // 4 rows, one per wave over all of K (1 token, K <= 4096)
+};
+DecodeKind decode_kind(int M, int K);
+int decode_rows(DecodeKind k);
+int decode_waves(DecodeKind k);
 
 // Unfused baseline kernels and helpers (elementwise.hip).
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);

@@ -150,7 +150,7 @@ hipError_t launch_norm_rows(int dtype, void* out, const void* gamma, const void*
 // The library's static device scratch (noalloc.hip): kScratchBytes per
 // device, for the split-K workspace of gemmepi_execute_noalloc.  Returns the
 // current device's address of it (looked up once per device).
-constexpr size_t kScratchBytes = (size_t)48 << 20;
+constexpr size_t kScratchBytes = (size_t)80 << 20;
 hipError_t scratch_pointer(void** ptr);
 
 // per-dtype launcher tables filled by each instantiation file

@@ -273,7 +273,7 @@ gemmepi_status_t gemmepi_execute_ws(gemmepi_plan_t plan, const void* A, const vo
  * capture, tight serving loops, harnesses that forbid hipMalloc): as
  * gemmepi_execute_ws, but a plan that splits K takes its workspace from a
  * static device array of the library, gemmepi_noalloc_scratch_bytes()
- * bytes (48 MiB) per device, which the code-object loader allocates when
+ * bytes (80 MiB) per device, which the code-object loader allocates when
  * the library's kernels are first loaded on a device and which stays
  * allocated until the process ends.  The call itself allocates nothing.
  * Its arrival counters are cleared by a fill kernel at the start of each

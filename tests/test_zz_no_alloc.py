@@ -81,16 +81,18 @@ def compare_noalloc_with_ws(c, splits=None, tile=-1, flags=0, label=""):
 
 
 def test_noalloc_two_calls_second_smaller():
-    """The 512-token FFN down-projection as planned (4 K ranges, 32 MiB of
-    partial tiles), then the BIAS workload W[1024,2048].X[2048,512] as
-    planned (2 K ranges, 4 MiB): the second call reuses the scratch that the
-    first left behind."""
-    _, down = wl.config2_ffn("b1s512")
-    # the down-projection's input is the up-projection's output; any
-    # [512, 11008] input serves this comparison
-    down.A = wl.normal((down.M, down.K), 7300, 1.0, down.dtype)
-    compare_noalloc_with_ws(down, flags=ge.FLAG_SPLIT_K, label="call 1")
-    compare_noalloc_with_ws(wl.config0_bias(), flags=ge.FLAG_SPLIT_K, label="call 2")
+    """The split plans of the suite as planned, each call smaller than the
+    one before and reusing the scratch it left behind: the 2048-token FFN
+    down-projection (256 x 256 tiles, 2 K ranges, 64 MiB of partial tiles),
+    the 512-token one (4 K ranges, 32 MiB), then the BIAS workload
+    W[1024,2048].X[2048,512] (2 K ranges, 4 MiB)."""
+    for i, v in enumerate(("b1s2048", "b1s512")):
+        _, down = wl.config2_ffn(v)
+        # the down-projection's input is the up-projection's output; any
+        # [tokens, 11008] input serves this comparison
+        down.A = wl.normal((down.M, down.K), 7300 + i, 1.0, down.dtype)
+        compare_noalloc_with_ws(down, flags=ge.FLAG_SPLIT_K, label=f"call {i + 1}")
+    compare_noalloc_with_ws(wl.config0_bias(), flags=ge.FLAG_SPLIT_K, label="call 3")
 
 
 @pytest.mark.parametrize("epi", list(O.EPILOGUES))

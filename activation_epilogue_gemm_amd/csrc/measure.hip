@@ -8,6 +8,11 @@
 // core bottleneck of LLM inference").  Its launch shape is a parameter, so
 // that the best rate over block sizes, loads in flight and cache policy is
 // the one reported.
+//
+// gemmepi_measure_mfma_loop runs the matrix-core work of the 256 x 256 GEMM
+// tile with no memory traffic at all: the rate the chip's power limit leaves
+// to the MFMAs alone, which the large fused GEMM is compared with beside the
+// published peak.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -17,6 +22,62 @@
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c, f16x8) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c, bf16x8) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+constexpr int kLoopWaves = 8;   // 2 per SIMD, as the 256 x 256 tile
+constexpr int kLoopFM = 8;      // 128 x 64 accumulators per wave: 8 x 4 blocks of 16 x 16
+constexpr int kLoopFN = 4;
+constexpr int kLoopFrags = kLoopFM + kLoopFN;
+
+// Wave w of every workgroup reads its 8 A and 4 B fragments (16 bytes per
+// lane each) from fragment slots [12 w, 12 w + 12) of src, then issues
+// `rounds` times the 32 MFMAs of one k step of the GEMM's 128 x 64 wave
+// tile, in its order: a snake over the blocks (along n for even rows of
+// blocks, back for odd ones), so consecutive MFMAs share one operand.  Lane
+// 0 of wave 0 stores the sum of its 128 accumulators into sink word
+// blockIdx % 1024, which keeps the work alive and lets a test count it.
+template <typename V>
+__global__ void __launch_bounds__(kLoopWaves * 64) mfma_loop_kernel(const u32x4* __restrict__ src,
+                                                                    float* sink, int rounds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  u32x4 a[kLoopFM], b[kLoopFN];
+#pragma unroll
+  for (int i = 0; i < kLoopFM; ++i) a[i] = src[(wave * kLoopFrags + i) * 64 + lane];
+#pragma unroll
+  for (int j = 0; j < kLoopFN; ++j) b[j] = src[(wave * kLoopFrags + kLoopFM + j) * 64 + lane];
+  f32x4 acc[kLoopFM][kLoopFN];
+#pragma unroll
+  for (int i = 0; i < kLoopFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kLoopFN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int fm = 0; fm < kLoopFM; ++fm)
+#pragma unroll
+      for (int f = 0; f < kLoopFN; ++f) {
+        const int fn = (fm & 1) ? kLoopFN - 1 - f : f;
+        acc[fm][fn] = mfma(b[fn], a[fm], acc[fm][fn], V{});
+      }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kLoopFM; ++i)
+#pragma unroll
+    for (int j = 0; j < kLoopFN; ++j) s += (acc[i][j][0] + acc[i][j][1]) + (acc[i][j][2] + acc[i][j][3]);
+  if (threadIdx.x == 0) sink[blockIdx.x & 1023] = s;
+}
 
 // Workgroup b reads the contiguous block [b * THREADS * LOADS, ...) of 16-byte
 // chunks, LOADS chunks per thread, all in flight before any is consumed.
@@ -65,6 +126,23 @@ hipError_t by_loads(int loads, const void* p, size_t n16, uint32_t* sink, int nt
 }
 
 }  // namespace
+
+extern "C" int gemmepi_measure_mfma_loop(const void* src, size_t src_bytes, void* sink, int blocks,
+                                         int rounds, int bf16, void* stream) {
+  if (!src || !sink || ((uintptr_t)src % 16) != 0 || ((uintptr_t)sink % 4) != 0) return 1;
+  if (src_bytes < (size_t)kLoopWaves * kLoopFrags * 64 * 16) return 1;
+  if (blocks < 1 || blocks > 65535 || rounds < 1 || rounds > (1 << 24)) return 1;
+  if (bf16 != 0 && bf16 != 1) return 1;
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  if (bf16)
+    hipLaunchKernelGGL(mfma_loop_kernel<bf16x8>, dim3(blocks), dim3(kLoopWaves * 64), 0, s,
+                       (const u32x4*)src, (float*)sink, rounds);
+  else
+    hipLaunchKernelGGL(mfma_loop_kernel<f16x8>, dim3(blocks), dim3(kLoopWaves * 64), 0, s,
+                       (const u32x4*)src, (float*)sink, rounds);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 extern "C" int gemmepi_measure_stream_read(const void* p, size_t bytes, void* sink, int threads,
                                            int loads, int nontemporal, void* stream) {

@@ -67,6 +67,9 @@ def parse():
                     help="only run the 1 GiB copy (calibration) and two fused executions of each "
                          "selected workload (--only, default c0,c2,c4), one after another, for "
                          "rocprofv3 --pmc runs of the tiles other than C3's")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only time the MFMA loop of the 256x256 tile with no memory traffic "
+                         "(fp16 and bf16, normal and zero operands) and print one JSON line each")
     ap.add_argument("--profile-decode", action="store_true",
                     help="only run the 1 GiB copy (calibration) and 16 decode calls each at "
                          "T = 1 and T = 16 over 16 rotated weight copies, for rocprofv3 --pmc runs")
@@ -89,6 +92,9 @@ def measure_library():
         lib.gemmepi_measure_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int,
                                                     ctypes.c_int, ctypes.c_int, vp]
         lib.gemmepi_measure_stream_read.restype = ctypes.c_int
+        lib.gemmepi_measure_mfma_loop.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int, vp]
+        lib.gemmepi_measure_mfma_loop.restype = ctypes.c_int
         _measure = lib
     return _measure
 
@@ -102,6 +108,66 @@ def stream_read(buf, nbytes, sink, threads=512, loads=16, nontemporal=0):
         torch.cuda.current_stream(buf.device).cuda_stream)
     if st != 0:
         raise RuntimeError(f"gemmepi_measure_stream_read failed with status {st}")
+
+
+MFMA_LOOP_WAVES, MFMA_LOOP_FRAGS = 8, 12   # per workgroup; 16-byte fragments per wave
+MFMA_LOOP_FLOP = 32 * 16384                # one round of a wave: 32 MFMAs 16x16x32
+
+
+def mfma_loop(src, sink, blocks, rounds, bf16):
+    """One launch of the MFMA loop of the measurement library on torch's
+    current stream (src: the 8 waves' operand fragments, >= 96 KiB)."""
+    import torch
+    st = measure_library().gemmepi_measure_mfma_loop(
+        src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(), int(blocks), int(rounds),
+        int(bf16), torch.cuda.current_stream(src.device).cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"gemmepi_measure_mfma_loop failed with status {st}")
+
+
+def mfma_loop_rate(dt="f16", kind="normal", trials=5, launches=5, rounds=40000):
+    """TFLOP/s of the MFMA loop of the 256x256 tile with no memory traffic
+    (one workgroup per CU), on standard-normal or zero operands: the median
+    (and minimum time) of `trials` trials of `launches` launches of ~20 ms,
+    timed with HIP events on torch's current stream."""
+    import statistics
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = MFMA_LOOP_WAVES * MFMA_LOOP_FRAGS * 64 * 8        # 8 halves per 16-byte fragment
+    sink = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    bf = 0 if dt == "f16" else 1
+    g = torch.Generator(device="cuda").manual_seed(7)
+    src = (torch.randn(n, device="cuda", generator=g) if kind == "normal"
+           else torch.zeros(n, device="cuda")).to(tdt)
+    flops = cus * MFMA_LOOP_WAVES * rounds * MFMA_LOOP_FLOP
+    mfma_loop(src, sink, cus, 100, bf)                     # warm-up
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            mfma_loop(src, sink, cus, rounds, bf)
+        e1.record()
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1) / launches)
+    med = statistics.median(ms)
+    return {"mfma_loop": dt, "operands": kind, "workgroups": cus, "rounds": rounds,
+            "ms_median": round(med, 4), "ms_min": round(min(ms), 4),
+            "tflops": round(flops / med / 1e9, 1),
+            "frac_of_published": round(flops / med / 1e9 / PEAK_TFLOPS, 4)}
+
+
+def mfma_ceiling():
+    """The matrix cores alone at the power limit: the 256x256 tile's MFMA
+    work (8 waves of 128x64 accumulators per CU) with no memory traffic, on
+    standard-normal and on zero operands, fp16 and bf16, one JSON line each."""
+    for dt in ("f16", "bf16"):
+        for kind in ("normal", "zero"):
+            rec = mfma_loop_rate(dt, kind)
+            print(json.dumps(rec), flush=True)
+            log(f"mfma loop {dt} {kind}: {rec['tflops']} TFLOP/s")
 
 
 # launch shapes of the stream-read sweep: (threads, loads per thread, non-temporal)
@@ -674,6 +740,11 @@ def main():
         torch.cuda.set_device(0)
         compare_blas(args.only)
         return
+    if args.mfma_ceiling:
+        import torch
+        torch.cuda.set_device(0)
+        mfma_ceiling()
+        return
     if args.profile_traffic or args.profile_decode or args.profile_layouts or args.profile_workloads:
         import torch  # noqa: F401
         import activation_epilogue_gemm_amd as ge
@@ -825,6 +896,14 @@ def main():
                 "implied_sclk_mhz": round(sclk) if sclk else None}
     log(f"roofline {dom.name}: {achieved:.1f} TFLOP/s = {achieved / PEAK_TFLOPS:.3f} of peak; "
         f"MFMA busy share {util}, implied shader clock {sclk and round(sclk)} MHz")
+    # context beside the published peak, measured after the timed steps on
+    # this same GPU: the tile's MFMA work alone at the power limit (fp16, normal
+    # operands, no memory traffic)
+    loop = mfma_loop_rate("f16", "normal", trials=3, launches=3)
+    roofline["mfma_loop_tflops"] = loop["tflops"]
+    roofline["frac_of_mfma_loop"] = round(achieved / loop["tflops"], 4)
+    log(f"mfma loop on this GPU: {loop['tflops']} TFLOP/s; the roofline kernel at "
+        f"{roofline['frac_of_mfma_loop']} of it")
 
     cpu = None
     if not args.no_cpu_baseline:

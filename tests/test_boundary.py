@@ -153,8 +153,8 @@ def test_execute_rejects_bad_pointers_before_any_hip_call():
 
 
 def test_measurement_helper_is_outside_the_gemm_library():
-    """The stream-read reference of the benchmark lives in its own library;
-    it validates its arguments before any HIP call."""
+    """The stream-read reference and the MFMA loop of the benchmark live in
+    their own library; they validate their arguments before any HIP call."""
     import bench
     assert not hasattr(ge.library(), "gemmepi_stream_read")
     m = bench.measure_library()
@@ -163,6 +163,16 @@ def test_measurement_helper_is_outside_the_gemm_library():
     assert m.gemmepi_measure_stream_read(4100, 4096, 4096, 512, 16, 0, None) == 1
     assert m.gemmepi_measure_stream_read(4096, 4096, 4096, 384, 16, 0, None) == 1
     assert m.gemmepi_measure_stream_read(4096, 4096, 4096, 512, 12, 0, None) == 1
+    # the MFMA loop: operands of the 8 waves (96 KiB), grid and round limits
+    assert m.gemmepi_measure_mfma_loop(None, 98304, 4096, 1, 1, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4096, 98303, 4096, 1, 1, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4104, 98304, 4096, 1, 1, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4096, 98304, None, 1, 1, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4096, 98304, 4096, 0, 1, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4096, 98304, 4096, 65536, 1, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4096, 98304, 4096, 1, 0, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4096, 98304, 4096, 1, (1 << 24) + 1, 0, None) == 1
+    assert m.gemmepi_measure_mfma_loop(4096, 98304, 4096, 1, 1, 2, None) == 1
 
 
 def test_binding_checks_tensor_arguments():

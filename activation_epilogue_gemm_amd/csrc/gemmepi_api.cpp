@@ -39,6 +39,21 @@ const TileCfg kTiles[kNumTiles] = {GEMMEPI_TILES(GEMMEPI_TILE_ENTRY)};
   static_assert(bm >= 64, "norm row counters: tile rows");
 GEMMEPI_TILES(GEMMEPI_TILE_ROWS)
 #undef GEMMEPI_TILE_ROWS
+// the deepest k slab and the most rows (of A, or of B stored [N,K]) that
+// one workgroup addresses from a single buffer descriptor
+#define GEMMEPI_TILE_BK(id, bm, bn, bk, wm, wn, ns, sched, mt) bk,
+#define GEMMEPI_TILE_MN(id, bm, bn, bk, wm, wn, ns, sched, mt) (bm > bn ? bm : bn),
+constexpr int kTileBk[] = {GEMMEPI_TILES(GEMMEPI_TILE_BK)};
+constexpr int kTileMn[] = {GEMMEPI_TILES(GEMMEPI_TILE_MN)};
+#undef GEMMEPI_TILE_BK
+#undef GEMMEPI_TILE_MN
+constexpr int max_of(const int* a, int n) {
+  int m = 0;
+  for (int i = 0; i < n; ++i) m = a[i] > m ? a[i] : m;
+  return m;
+}
+constexpr int kMaxSlabK = max_of(kTileBk, kNumTiles);
+constexpr int kMaxPanelRows = max_of(kTileMn, kNumTiles);
 
 // Relative throughput of one CU on a full tile of each configuration, and
 // how many of its workgroups fit on one CU (LDS and registers).  Used only
@@ -508,8 +523,10 @@ gemmepi_status_t make_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K
     return fail(GEMMEPI_ERR_MISALIGNED,
                 "N=%lld must be a multiple of 8 when B is stored [K,N] (no B_TRANS)",
                 (long long)N);
-  // 32-bit buffer offsets: a 256-row panel of A or of B must stay below 2 GiB
-  if (K * 2 * 256 >= 0x7FFFFFF0LL || (!bt && N * 2 * 64 >= 0x7FFFFFF0LL))
+  // 32-bit buffer offsets: the rows of A (or of B stored [N,K]) that one
+  // workgroup addresses, and the k rows of one slab of B stored [K,N], must
+  // stay below 2 GiB from the descriptor's base, whatever tile runs
+  if (K * 2 * kMaxPanelRows >= 0x7FFFFFF0LL || (!bt && N * 2 * kMaxSlabK >= 0x7FFFFFF0LL))
     return fail(GEMMEPI_ERR_UNSUPPORTED, "leading dimension too large (K=%lld N=%lld)",
                 (long long)K, (long long)N);
   if (M * N > (int64_t)1 << 40)

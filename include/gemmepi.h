@@ -152,7 +152,11 @@ typedef struct gemmepi_plan_s* gemmepi_plan_t;
  *   flags  OR of GEMMEPI_FLAG_*
  *
  * Errors: INVALID_VALUE (null plan, sizes, unknown enum/flag bits),
- * MISALIGNED (K or N not a multiple of 8 as above), NO_MEMORY.
+ * MISALIGNED (K or N not a multiple of 8 as above), UNSUPPORTED for
+ * shapes past the kernels' 32-bit buffer offsets (K >= 2^22, or N >= 2^23
+ * with B stored [K,N]: 256 K-contiguous rows, or the 128 k rows of the
+ * deepest slab of B, must span less than 2 GiB) or with M * N > 2^40,
+ * NO_MEMORY.
  */
 gemmepi_status_t gemmepi_plan(gemmepi_plan_t* plan, int64_t M, int64_t N, int64_t K,
                               gemmepi_dtype_t dtype, gemmepi_epilogue_t epi, uint32_t flags);

@@ -62,6 +62,14 @@ def test_plan_validation():
     assert _plan_status(64, 60, 64) == ge.ERR_MISALIGNED          # N % 8 without B_TRANS
     assert "N=60" in ge.last_error()
     assert _plan_status(64, 60, 64, flags=ge.FLAG_B_TRANS) == ge.OK
+    # 32-bit buffer offsets: 256 rows of K-contiguous operand, or 128 k rows
+    # (the deepest slab, tile 9) of B stored [K,N], must span less than 2 GiB
+    assert _plan_status(64, 64, 1 << 22) == ge.ERR_UNSUPPORTED
+    assert _plan_status(64, 64, (1 << 22) - 8) == ge.OK
+    assert _plan_status(64, 1 << 23, 64) == ge.ERR_UNSUPPORTED
+    assert "leading dimension" in ge.last_error()
+    assert _plan_status(64, (1 << 23) - 8, 64) == ge.OK
+    assert _plan_status(64, 1 << 23, 64, flags=ge.FLAG_B_TRANS) == ge.OK
     lib = ge.library()
     assert lib.gemmepi_plan(None, 1, 1, 8, 0, 0, 0) == ge.ERR_INVALID_VALUE
 

@@ -369,12 +369,22 @@ __global__ void __launch_bounds__(256) gemv_rowwave_kernel(const DecodeArgs p) {
 // tokens, and the VALU products grow with M).  Rows per workgroup, interleaved on one box
 // (M = 1 / 2 / 3 / 4): 4 rows 7.03 / 7.26 / 8.12 / 8.22 us, 8 rows 7.17 /
 // 7.47 / 8.78 / 8.47, 2 rows 7.00 / 7.65 / 8.67 / 9.45.
+// Four tokens stay on the MFMA kernel only while it runs in one round of
+// one 16-row workgroup per CU (N <= 16 x 256) with one 512-wide k window per
+// wave (K <= 8 x 512); past that its workgroups queue for a second round, or
+// each wave walks its windows one after another, and the row-streaming
+// kernel is faster.  Four tokens over rotated weights, interleaved on one
+// box, MFMA against row streaming: 7.95 against 8.18 us at N = K = 4096,
+// but 18.89 against 17.94 at N 4096 x K 11008, 19.65 against 17.10 at
+// N 11008 x K 4096 and 20.72 against 18.83 at N 12288 x K 4096.
 #ifndef GEMMEPI_GEMV_ROWS
 #define GEMMEPI_GEMV_ROWS 4
 #endif
-DecodeKind decode_kind(int M, int K) {
+DecodeKind decode_kind(int M, int N, int K) {
   if (M == 1 && K <= 4096) return DECODE_ROWWAVE;
-  return M <= 3 ? DECODE_ROWSTREAM : DECODE_MFMA;
+  if (M <= 3) return DECODE_ROWSTREAM;
+  if (M == 4 && (N > 16 * 256 || K > kDecodeWaves * kDecodeWin)) return DECODE_ROWSTREAM;
+  return DECODE_MFMA;
 }
 int decode_rows(DecodeKind k) {
   return k == DECODE_MFMA ? 16 : (k == DECODE_ROWSTREAM ? GEMMEPI_GEMV_ROWS : 4);
@@ -409,7 +419,7 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s) {
   if (a.M < 1 || a.M > 16) return hipErrorInvalidValue;
-  const DecodeKind kind = a.K % 8 == 0 ? decode_kind(a.M, a.K) : DECODE_MFMA;
+  const DecodeKind kind = a.K % 8 == 0 ? decode_kind(a.M, a.N, a.K) : DECODE_MFMA;
   if (kind == DECODE_ROWWAVE) {
     const dim3 grid((a.N + 3) / 4), block(256);
     if (dtype == DT_F16)

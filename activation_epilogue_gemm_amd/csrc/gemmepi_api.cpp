@@ -317,7 +317,7 @@ void describe(gemmepi_plan_s* p) {
                                "BIAS_RES_RMSNORM", "BIAS_RES_LAYERNORM",
                                "GELU_AUX_BIAS", "DGELU_BGRAD"};
   if (p->path == PATH_DECODE) {
-    const DecodeKind kind = decode_kind((int)p->M, (int)p->K);
+    const DecodeKind kind = decode_kind((int)p->M, (int)p->N, (int)p->K);
     const int rows = decode_rows(kind);
     static const char* kinds[] = {"mfma", "rowstream", "rowwave"};
     snprintf(buf, sizeof(buf),

@@ -112,14 +112,15 @@ constexpr uint32_t kNormWaitPolls = 1u << 21;
 // (hipOccupancyMaxActiveBlocksPerMultiprocessor).
 hipError_t gemm_blocks_per_cu(int dtype, bool b_trans, int tile, int* n);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t s);
-// The decode kernel for M tokens and reduction length K, and its launch
-// shape (rows of W per workgroup, waves per workgroup).
+// The decode kernel for M tokens, N rows of W and reduction length K, and
+// its launch shape (rows of W per workgroup, waves per workgroup).
 enum DecodeKind : int {
   DECODE_MFMA = 0,       // 16 rows of W per workgroup, MFMA products (4-16 tokens)
-  DECODE_ROWSTREAM = 1,  // 4 rows, 8 waves splitting K, VALU products (1-3 tokens)
+  DECODE_ROWSTREAM = 1,  // 4 rows, 8 waves splitting K, VALU products (1-3 tokens;
+                         // 4 when N > 4096 or K > 4096)
   DECODE_ROWWAVE = 2     // 4 rows, one per wave over all of K (1 token, K <= 4096)
 };
-DecodeKind decode_kind(int M, int K);
+DecodeKind decode_kind(int M, int N, int K);
 int decode_rows(DecodeKind k);
 int decode_waves(DecodeKind k);
 

@@ -99,6 +99,13 @@ def test_plan_cache_and_refcount():
 def test_plan_paths_and_tiles():
     with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", ge.FLAG_B_TRANS | ge.FLAG_BIAS_PER_COL) as p:
         assert "path=decode" in p.info()
+    # the decode kernel by token count and weight shape
+    for (M, N, K, kind) in ((1, 4096, 4096, "rowwave"), (1, 4096, 11008, "rowstream"),
+                            (3, 4096, 4096, "rowstream"), (4, 4096, 4096, "mfma"),
+                            (4, 11008, 4096, "rowstream"), (4, 4096, 11008, "rowstream"),
+                            (5, 11008, 4096, "mfma"), (16, 4096, 4096, "mfma")):
+        with ge.plan(M, N, K, "f16", "GELU_BIAS", ge.FLAG_B_TRANS | ge.FLAG_BIAS_PER_COL) as p:
+            assert f"kernel={kind} " in p.info(), (M, N, K, p.info())
     with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", ge.FLAG_B_TRANS | ge.FLAG_NO_DECODE) as p:
         assert "path=gemm" in p.info()
     with ge.plan(4, 4096, 4096, "f16", "GELU_BIAS", 0) as p:   # B not transposed: no decode

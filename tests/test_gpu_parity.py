@@ -132,7 +132,9 @@ def test_unfused_matches_oracle(epi, dtype):
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_decode_path(T, dtype):
     for epi in ("DEFAULT", "BIAS", "RELU_BIAS", "GELU_BIAS"):
-        for (N, K) in ((200, 520), (4096, 4096), (24, 8), (203, 4104), (203, 1000)):
+        # (4104, 520): N past 4096 rows, where four tokens take the
+        # row-streaming kernel as they do with K past 4096 (203, 4104)
+        for (N, K) in ((200, 520), (4096, 4096), (24, 8), (203, 4104), (203, 1000), (4104, 520)):
             c = wl.random_case(T, N, K, dtype, epi, True, True, 300 + T + N)
             r = GpuRun(c)
             assert "path=decode" in r.info, r.info

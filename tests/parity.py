@@ -81,7 +81,7 @@ def flags_of(case, extra: int = 0) -> int:
     return f
 
 
-class GpuRun:
+class DeviceRun:
     """Device buffers and results of one execution of a GemmCase."""
 
     def __init__(self, case, flags: int = 0, tile: int = -1, A_dev=None, guard: int = 0,

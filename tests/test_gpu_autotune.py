@@ -8,7 +8,7 @@ import pytest
 
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
-from parity import GpuRun, check_mask, check_out
+from parity import DeviceRun, check_mask, check_out
 from oracle import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -20,7 +20,7 @@ def test_autotune_picks_the_fastest_tile_and_persists(tmp_path):
     os.environ["GEMMEPI_TUNE_CACHE"] = str(path)
     try:
         c = wl.random_case(1040, 1552, 520, "f16", "RELU_AUX_BIAS", False, False, 4242)
-        r = GpuRun(c)
+        r = DeviceRun(c)
         p = ge.plan(c.M, c.N, c.K, "f16", "RELU_AUX_BIAS", 0)
         before = p.info()
         times = p.autotune(r.A, r.B, r.bias, r.aux, r.out, reps=3)

@@ -8,7 +8,7 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import GpuRun, check_out
+from parity import DeviceRun, check_out
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def test_long_k(b_trans):
     rows = wl.sample_rows(c.M, 16, 9199)
     ref = _ref(c, rows)
     for splits in (None, 8, 64):
-        r = GpuRun(c, splits=splits)
+        r = DeviceRun(c, splits=splits)
         say(c.name, splits, r.info)
         r.run()
         check_out(c, r.out_bits(rows), ref, label=f"{c.name}-splits{splits}")
@@ -59,7 +59,7 @@ def test_wide_n_deepest_slab():
     deep = [t for t in range(ge.num_tiles()) if ge.tile_name(t).startswith("64x64x128")]
     assert deep, "no 64x64x128 tile"
     for tile in (-1, deep[0]):
-        r = GpuRun(c, tile=tile)
+        r = DeviceRun(c, tile=tile)
         say(c.name, tile, r.info)
         r.run()
         got = r.out_bits(rows)

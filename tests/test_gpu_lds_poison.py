@@ -50,7 +50,7 @@ def poisoned():
 
 
 def exact(c, flags=0, tile=-1, splits=None):
-    r = parity.GpuRun(c, flags=flags, tile=tile, guard=64, splits=splits)
+    r = parity.DeviceRun(c, flags=flags, tile=tile, guard=64, splits=splits)
     r.run()
     ref = O.gemm_epilogue(c.A, c.B, c.bias, c.aux, c.M, c.N, c.K, c.dtype, c.epilogue, c.b_trans,
                           c.bias_per_col)

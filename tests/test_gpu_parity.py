@@ -17,7 +17,7 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check_out, check_zaux
+from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, DeviceRun, check_bgrad, check_mask, check_out, check_zaux
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def run_and_check(c, flags=0, tile=-1, exact=False, guard=0, label=""):
     """exact: integer inputs, so every result that is a rounding of an exact
     sum is compared bit for bit; results that go through GELU or its
     derivative (out of the GELU epilogues, DGELU's bgrad) use the tolerance."""
-    r = GpuRun(c, flags=flags, tile=tile, guard=guard)
+    r = DeviceRun(c, flags=flags, tile=tile, guard=guard)
     say(label, c.name, r.info)
     r.run()
     ref = oracle_of(c)
@@ -136,7 +136,7 @@ def test_decode_path(T, dtype):
         # row-streaming kernel as they do with K past 4096 (203, 4104)
         for (N, K) in ((200, 520), (4096, 4096), (24, 8), (203, 4104), (203, 1000), (4104, 520)):
             c = wl.random_case(T, N, K, dtype, epi, True, True, 300 + T + N)
-            r = GpuRun(c)
+            r = DeviceRun(c)
             assert "path=decode" in r.info, r.info
             r.close()
             run_and_check(c, guard=32, label="decode")
@@ -164,7 +164,7 @@ def test_edge_shapes(shape):
 
 def test_repeatable_and_stable():
     c = wl.random_case(512, 512, 512, "f16", "RELU_AUX_BIAS", False, False, 42)
-    r = GpuRun(c).run()
+    r = DeviceRun(c).run()
     o1, a1 = r.out_bits(), r.aux_words()
     r.run(times=3)
     assert np.array_equal(o1, r.out_bits()) and np.array_equal(a1, r.aux_words())
@@ -194,11 +194,11 @@ def test_config2_ffn_full(variant):
     down.A = ref_up.out
     ref_chain = oracle_of(down)
     for flags in (0, ge.FLAG_UNFUSED):
-        ru = GpuRun(up, flags=flags).run()
+        ru = DeviceRun(up, flags=flags).run()
         say("config2", variant, ru.info)
         h_gpu = ru.out_bits()
         check_out(up, h_gpu, ref_up, label=f"config2-up-{flags}")
-        rd = GpuRun(down, flags=flags, A_dev=ru.out).run()
+        rd = DeviceRun(down, flags=flags, A_dev=ru.out).run()
         say("config2", variant, rd.info)
         y_gpu = rd.out_bits()
         check_out(down, y_gpu, oracle_of(down, A_bits=h_gpu), A_bits=h_gpu,
@@ -222,7 +222,7 @@ def _large(c, rows_count=4096, flag_sets=(0, ge.FLAG_UNFUSED)):
         ref = O.gemm_epilogue(c.host_A(rows), B, c.bias[rows], None, len(rows), c.N, c.K,
                               c.dtype, c.epilogue, c.b_trans, c.bias_per_col)
     for flags in flag_sets:
-        r = GpuRun(c, flags=flags)
+        r = DeviceRun(c, flags=flags)
         say("large", c.name, r.info)
         if flags & ge.FLAG_STAGE_B:
             assert "stage_b" in r.info, r.info

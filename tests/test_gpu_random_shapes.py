@@ -17,7 +17,7 @@ import pytest
 import workloads as wl
 from oracle import oracle as O
 import activation_epilogue_gemm_amd as ge
-from parity import (NUM_TILES, BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_norm, check_out,
+from parity import (NUM_TILES, BGRAD_EPIS, GELU_EPIS, DeviceRun, check_bgrad, check_norm, check_out,
                     check_zaux, run_norm)
 
 pytestmark = pytest.mark.gpu
@@ -46,7 +46,7 @@ def test_random_cases_match_the_oracle(chunk):
         if i % 4 != chunk:
             continue
         c = wl.random_case(M, N, K, dtype, epi, b_trans, per_col, 50000 + i, kind="int")
-        r = GpuRun(c, tile=tile, splits=splits, guard=32)
+        r = DeviceRun(c, tile=tile, splits=splits, guard=32)
         print(f"[random] case {i}: {r.info}", file=sys.stderr, flush=True)
         r.run()
         ref = O.gemm_epilogue(c.A, c.B, c.bias, c.aux, M, N, K, dtype, epi, b_trans, per_col)
@@ -97,7 +97,7 @@ def test_wide_random_cases_match_the_oracle(chunk):
         if i % 3 != chunk:
             continue
         c = wl.random_case(M, N, K, dtype, epi, b_trans, per_col, 700000 + i, kind=kind)
-        r = GpuRun(c, flags=flags, tile=tile, splits=splits, guard=32)
+        r = DeviceRun(c, flags=flags, tile=tile, splits=splits, guard=32)
         print(f"[random-wide] case {i} ({kind}): {r.info}", file=sys.stderr, flush=True)
         r.run()
         ref = O.gemm_epilogue(c.A, c.B, c.bias, c.aux, M, N, K, dtype, epi, b_trans, per_col)

@@ -14,7 +14,7 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_mask, check_out, check_zaux
+from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, DeviceRun, check_bgrad, check_mask, check_out, check_zaux
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def oracle_of(c):
 
 
 def run_and_check(c, splits, flags=0, tile=-1, exact=False, guard=0, label=""):
-    r = GpuRun(c, flags=flags, tile=tile, guard=guard, splits=splits)
+    r = DeviceRun(c, flags=flags, tile=tile, guard=guard, splits=splits)
     say(label, c.name, r.info)
     r.run()
     ref = oracle_of(c)
@@ -99,7 +99,7 @@ def test_repeatable_and_workspace_reuse():
     a plan with another tile count reuses it right after."""
     import torch
     c = wl.random_case(512, 640, 2048, "f16", "RELU_AUX_BIAS", False, False, 3700)
-    r = GpuRun(c, splits=4, tile=3)
+    r = DeviceRun(c, splits=4, tile=3)
     need = r.plan.workspace_bytes()
     assert need > 0
     ws = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
@@ -118,7 +118,7 @@ def test_repeatable_and_workspace_reuse():
     assert int(ws[:4 * ntiles].view(torch.int32).abs().sum()) == 0
     r.close()
     c2 = wl.random_case(300, 264, 1000, "f16", "GELU_BIAS", True, True, 3701)
-    r2 = GpuRun(c2, splits=5, tile=5)
+    r2 = DeviceRun(c2, splits=5, tile=5)
     assert r2.plan.workspace_bytes() <= ws.numel()
     r2.plan.execute(r2.A, r2.B, r2.bias, None, r2.out, workspace=ws)
     torch.cuda.synchronize()
@@ -129,7 +129,7 @@ def test_repeatable_and_workspace_reuse():
 def test_split_plan_needs_a_workspace():
     import torch
     c = wl.random_case(256, 256, 512, "f16", "BIAS", False, False, 3800)
-    r = GpuRun(c, splits=2, tile=3)
+    r = DeviceRun(c, splits=2, tile=3)
     lib = ge.library()
     st = lib.gemmepi_execute(r.plan._h, r.A.data_ptr(), r.B.data_ptr(), r.bias.data_ptr(), None,
                              r.out.data_ptr(), None)
@@ -170,7 +170,7 @@ def test_first_execution_enqueued_on_another_stream():
     output would be left as it was."""
     import torch
     c = wl.random_case(300, 264, 600, "f16", "RELU_BIAS", False, False, 3950, kind="int")
-    r = GpuRun(c, tile=5, splits=3)
+    r = DeviceRun(c, tile=5, splits=3)
     s = torch.cuda.Stream()
     r.out.view(torch.int16).fill_(0x7E00)
     torch.cuda.synchronize()
@@ -193,7 +193,7 @@ def test_split_k_arrivals_over_many_rounds():
     import torch
     M, N, K = 4096, 4096, 1024
     c = wl.random_case(M, N, K, "f16", "BIAS", False, False, 3900, kind="int")
-    r = GpuRun(c, tile=5, splits=8)
+    r = DeviceRun(c, tile=5, splits=8)
     say("many rounds", r.info)
     assert "splits=8" in r.info
     ref = O.gemm_epilogue(c.A, c.B, c.bias, None, M, N, K, "f16", "BIAS", False, False)

@@ -13,7 +13,7 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, GpuRun, check_bgrad, check_out
+from parity import NUM_TILES, BGRAD_EPIS, GELU_EPIS, DeviceRun, check_bgrad, check_out
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def outputs(r):
 
 
 def run(c, flags, tile=-1):
-    r = GpuRun(c, flags=flags, tile=tile, guard=64)
+    r = DeviceRun(c, flags=flags, tile=tile, guard=64)
     r.run()
     res = outputs(r)
     assert r.guards_intact(), f"{c.name} [{r.info}]: write outside the output buffers"

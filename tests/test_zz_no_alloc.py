@@ -14,7 +14,7 @@ import pytest
 import activation_epilogue_gemm_amd as ge
 import workloads as wl
 from oracle import oracle as O
-from parity import GpuRun, check_bgrad
+from parity import DeviceRun, check_bgrad
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +53,7 @@ def compare_noalloc_with_ws(c, splits=None, tile=-1, flags=0, label=""):
     workspace), then through gemmepi_execute_noalloc into the same, poisoned,
     buffers; every output must be bitwise identical."""
     import torch
-    r = GpuRun(c, flags=flags, tile=tile, guard=64, splits=splits)
+    r = DeviceRun(c, flags=flags, tile=tile, guard=64, splits=splits)
     need = r.plan.workspace_bytes()
     say(label, c.name, r.info, f"workspace {need} bytes")
     assert 0 < need <= ge.noalloc_scratch_bytes(), (need, r.info)
@@ -108,7 +108,7 @@ def test_noalloc_every_epilogue_integer(epi):
 def test_noalloc_unsplit_plan_equals_execute():
     import torch
     c = wl.random_case(200, 136, 96, "bf16", "RELU_AUX_BIAS", False, False, 7200)
-    r = GpuRun(c, guard=64)
+    r = DeviceRun(c, guard=64)
     assert r.plan.workspace_bytes() == 0
     r.run()
     want = results(r)

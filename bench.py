@@ -900,10 +900,18 @@ def main():
     # this same GPU: the tile's MFMA work alone at the power limit (fp16, normal
     # operands, no memory traffic)
     loop = mfma_loop_rate("f16", "normal", trials=3, launches=3)
+    loop_bf16 = mfma_loop_rate("bf16", "normal", trials=3, launches=3)
     roofline["mfma_loop_tflops"] = loop["tflops"]
     roofline["frac_of_mfma_loop"] = round(achieved / loop["tflops"], 4)
-    log(f"mfma loop on this GPU: {loop['tflops']} TFLOP/s; the roofline kernel at "
-        f"{roofline['frac_of_mfma_loop']} of it")
+    log(f"mfma loop on this GPU: {loop['tflops']} TFLOP/s (bf16 {loop_bf16['tflops']}); the "
+        f"roofline kernel at {roofline['frac_of_mfma_loop']} of it")
+    # every GEMM workload beside the loop of its own dtype (the decode shapes
+    # are bound by HBM and carry their stream-read fraction instead)
+    for w in suite + extras:
+        e = per[w.name]
+        if "gbs" not in e:
+            ref = loop_bf16 if w.case.dtype == "bf16" else loop
+            e["frac_of_mfma_loop"] = round(e["tflops"] / ref["tflops"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -944,12 +944,13 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   }
 
   // ---- split-K: partial tiles through the workspace ---------------------------
-  // Each split writes its fp32 accumulators to its slot, element-major
-  // (element q of thread t at q * NT + t, so each store or load of a wave is
-  // one contiguous 256 bytes).  The slot is written and read with
-  // agent-scope atomic stores and loads, which are coherent across the XCDs'
-  // L2 caches on their own; a fence would instead write back and invalidate
-  // the whole L2 of the XCD, which measured ~0.7 us per workgroup.  A split
+  // Each split writes its fp32 accumulators to its slot of the workspace.
+  // The slot is written and read with the agent-scope coherence bit, which
+  // keeps the accesses coherent across the XCDs' L2 caches on their own; a
+  // fence would instead write back and invalidate the whole L2 of the XCD,
+  // which measured ~0.7 us per workgroup.  (Agent-scope atomic loads and
+  // stores carry the same bit but move 4 bytes per lane; 16 per lane
+  // measured up to 5 % faster on split-K launches.)  A split
   // waits for its stores to complete, then counts its arrival; the split
   // that arrives last sums all slots in split order (the result does not
   // depend on arrival order), resets the count and runs the epilogue.
@@ -957,16 +958,27 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
   // can stall the grid.
   if (p.splits > 1) {
     constexpr int QE = FM * FN * kAccN;  // floats per thread
+    constexpr int G4 = kAccN / 4;        // 16-byte groups per accumulator block
+    // A slot holds group g (4 consecutive elements of a block) of thread t at
+    // bytes 16 (g NT + t): each store or load of a wave is one contiguous
+    // 1 KiB.  The accesses carry the agent-scope coherence bit (sc1, the bit
+    // agent-scope atomics are built with), 16 bytes per lane.
+    constexpr int kSc1 = 16;
     float* const slots = p.ws + (size_t)tile_id * p.splits * (BM * BN);
-    float* const own = slots + (size_t)split * (QE * NT);
+    const __amdgpu_buffer_rsrc_t rslot = make_rsrc(slots);
+    auto slot_off = [&](int s, int blk, int g4) -> uint32_t {
+      return (uint32_t)s * (QE * NT * 4u) + (uint32_t)((blk * G4 + g4) * NT + tid) * 16u;
+    };
     static_for<FM>([&](auto fm_c) {
       constexpr int fm = decltype(fm_c)::value;
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int r = 0; r < kAccN; ++r)
-          __hip_atomic_store(own + ((fm * FN + fn) * kAccN + r) * NT + tid, acc[fm][fn][r],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g4 = 0; g4 < G4; ++g4) {
+          const u32x4 w = {__float_as_uint(acc[fm][fn][4 * g4]), __float_as_uint(acc[fm][fn][4 * g4 + 1]),
+                           __float_as_uint(acc[fm][fn][4 * g4 + 2]), __float_as_uint(acc[fm][fn][4 * g4 + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rslot, slot_off(split, fm * FN + fn, g4), 0, kSc1);
+        }
     });
     wait_vmcnt<0>();  // this thread's slot stores are complete
     __syncthreads();  // ... and every thread's
@@ -984,7 +996,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     const uint32_t is_last = s_last;
     __syncthreads();  // every thread has read the flag before the epilogue reuses the ring
     if (is_last == 0u) return;  // uniform over the workgroup
-    // one slot per pass, in steps of 16 or 32 independent loads (hoisting
+    // one slot per pass, in steps of 16 or 32 floats per thread (hoisting
     // all loads of a slot would spill the accumulators)
     constexpr int FNG = kAccN == 16 ? (FN > 2 ? 1 : FN) : (FN > 4 ? 4 : FN);  // blocks per step
     static_assert(FN % FNG == 0, "split-K load steps");
@@ -997,7 +1009,6 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     // split arrived last.  The loads of each step are issued one step
     // ahead.  (On the 256-wide tiles a second path here costs spills.)
     if (kAccN == 16 && p.splits == 2) {
-      const float* src = slots + (size_t)(1 - split) * (QE * NT);
       constexpr bool kAhead = true;
       constexpr int NF = FN / FNG, NSTEP = FM * NF;
       float v[kAhead ? 2 : 1][FNG][kAccN];
@@ -1007,9 +1018,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
         for (int j = 0; j < FNG; ++j)
 #pragma unroll
-          for (int r = 0; r < kAccN; ++r)
-            v[b][j][r] = __hip_atomic_load(src + ((fm * FN + f0 + j) * kAccN + r) * NT + tid,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int g4 = 0; g4 < G4; ++g4) {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                rslot, slot_off(1 - split, fm * FN + f0 + j, g4), 0, kSc1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[b][j][4 * g4 + e] = __uint_as_float(w[e]);
+          }
       };
       if constexpr (kAhead) issue(std::integral_constant<int, 0>{});
       const bool first = split == 0;
@@ -1029,9 +1043,44 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           }
         __builtin_amdgcn_sched_barrier(0);
       });
+    } else if constexpr (QE <= 64 && (FM * (FN / FNG)) % 2 == 0) {
+      // tiles with at most 64 accumulators per thread: the slots in split
+      // order, each step's loads issued one step ahead (into the other of two
+      // register sets; a slot has an even number of steps, so a step's set is
+      // the same in every slot), the next slot's first step after a slot's
+      // last.  (The second set makes the 256-wide tiles spill.)
+      constexpr int NF = FN / FNG, SPS = FM * NF;
+      float v[2][FNG][kAccN];
+      auto load = [&](int s, int fm, int f0, float (&dst)[FNG][kAccN]) {
+#pragma unroll
+        for (int j = 0; j < FNG; ++j)
+#pragma unroll
+          for (int g4 = 0; g4 < G4; ++g4) {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                rslot, slot_off(s, fm * FN + f0 + j, g4), 0, kSc1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[j][4 * g4 + e] = __uint_as_float(w[e]);
+          }
+      };
+      load(0, 0, 0, v[0]);
+      for (int s = 0; s < p.splits; ++s) {
+        static_for<SPS>([&](auto st_c) {
+          constexpr int st = decltype(st_c)::value;
+          constexpr int fm = st / NF, f0 = (st % NF) * FNG, b = st & 1;
+          if constexpr (st + 1 < SPS)
+            load(s, (st + 1) / NF, ((st + 1) % NF) * FNG, v[b ^ 1]);
+          else if (s + 1 < p.splits)
+            load(s + 1, 0, 0, v[b ^ 1]);
+#pragma unroll
+          for (int j = 0; j < FNG; ++j)
+#pragma unroll
+            for (int r = 0; r < kAccN; ++r)
+              acc[fm][f0 + j][r] = (s == 0 ? 0.0f : acc[fm][f0 + j][r]) + v[b][j][r];
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
     } else
     for (int s = 0; s < p.splits; ++s) {
-      const float* src = slots + (size_t)s * (QE * NT);
       static_for<FM>([&](auto fm_c) {
         constexpr int fm = decltype(fm_c)::value;
 #pragma unroll
@@ -1040,9 +1089,12 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
 #pragma unroll
           for (int j = 0; j < FNG; ++j)
 #pragma unroll
-            for (int r = 0; r < kAccN; ++r)
-              v[j][r] = __hip_atomic_load(src + ((fm * FN + f0 + j) * kAccN + r) * NT + tid,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int g4 = 0; g4 < G4; ++g4) {
+              const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                  rslot, slot_off(s, fm * FN + f0 + j, g4), 0, kSc1);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[j][4 * g4 + e] = __uint_as_float(w[e]);
+            }
 #pragma unroll
           for (int j = 0; j < FNG; ++j)
 #pragma unroll

@@ -1048,10 +1048,20 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       // order, each step's loads issued one step ahead (into the other of two
       // register sets; a slot has an even number of steps, so a step's set is
       // the same in every slot), the next slot's first step after a slot's
-      // last.  (The second set makes the 256-wide tiles spill.)
+      // last.  This split's own term comes from a copy of its accumulators
+      // instead of its slot.  (The second set makes the 256-wide tiles spill.)
       constexpr int NF = FN / FNG, SPS = FM * NF;
+      float own[FM][FN][kAccN];
+      static_for<FM>([&](auto fm_c) {
+        constexpr int fm = decltype(fm_c)::value;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+          for (int r = 0; r < kAccN; ++r) own[fm][fn][r] = acc[fm][fn][r];
+      });
       float v[2][FNG][kAccN];
       auto load = [&](int s, int fm, int f0, float (&dst)[FNG][kAccN]) {
+        if (s == split) return;  // uniform: the own term is in registers
 #pragma unroll
         for (int j = 0; j < FNG; ++j)
 #pragma unroll
@@ -1064,6 +1074,7 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
       };
       load(0, 0, 0, v[0]);
       for (int s = 0; s < p.splits; ++s) {
+        const bool mine = s == split;
         static_for<SPS>([&](auto st_c) {
           constexpr int st = decltype(st_c)::value;
           constexpr int fm = st / NF, f0 = (st % NF) * FNG, b = st & 1;
@@ -1075,31 +1086,48 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
           for (int j = 0; j < FNG; ++j)
 #pragma unroll
             for (int r = 0; r < kAccN; ++r)
-              acc[fm][f0 + j][r] = (s == 0 ? 0.0f : acc[fm][f0 + j][r]) + v[b][j][r];
+              acc[fm][f0 + j][r] =
+                  (s == 0 ? 0.0f : acc[fm][f0 + j][r]) + (mine ? own[fm][f0 + j][r] : v[b][j][r]);
           __builtin_amdgcn_sched_barrier(0);
         });
       }
-    } else
-    for (int s = 0; s < p.splits; ++s) {
+    } else {
+      // every other tile shape: step by step, the sum over the slots in split
+      // order, this split's own term taken from its accumulators rather than
+      // read back from its slot (each element still sums the same terms in
+      // the same order)
       static_for<FM>([&](auto fm_c) {
         constexpr int fm = decltype(fm_c)::value;
 #pragma unroll
         for (int f0 = 0; f0 < FN; f0 += FNG) {
-          float v[FNG][kAccN];
+          float t[FNG][kAccN];
+          for (int s = 0; s < p.splits; ++s) {
+            float v[FNG][kAccN];
+            if (s == split) {
 #pragma unroll
-          for (int j = 0; j < FNG; ++j)
+              for (int j = 0; j < FNG; ++j)
 #pragma unroll
-            for (int g4 = 0; g4 < G4; ++g4) {
-              const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
-                  rslot, slot_off(s, fm * FN + f0 + j, g4), 0, kSc1);
+                for (int r = 0; r < kAccN; ++r) v[j][r] = acc[fm][f0 + j][r];
+            } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) v[j][4 * g4 + e] = __uint_as_float(w[e]);
+              for (int j = 0; j < FNG; ++j)
+#pragma unroll
+                for (int g4 = 0; g4 < G4; ++g4) {
+                  const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+                      rslot, slot_off(s, fm * FN + f0 + j, g4), 0, kSc1);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) v[j][4 * g4 + e] = __uint_as_float(w[e]);
+                }
             }
 #pragma unroll
+            for (int j = 0; j < FNG; ++j)
+#pragma unroll
+              for (int r = 0; r < kAccN; ++r) t[j][r] = (s == 0 ? 0.0f : t[j][r]) + v[j][r];
+          }
+#pragma unroll
           for (int j = 0; j < FNG; ++j)
 #pragma unroll
-            for (int r = 0; r < kAccN; ++r)
-              acc[fm][f0 + j][r] = (s == 0 ? 0.0f : acc[fm][f0 + j][r]) + v[j][r];
+            for (int r = 0; r < kAccN; ++r) acc[fm][f0 + j][r] = t[j][r];
           __builtin_amdgcn_sched_barrier(0);
         }
       });

@@ -996,14 +996,14 @@ __global__ void __launch_bounds__(WM * WN * 64, 1) gemm_kernel(const GemmArgs p)
     const uint32_t is_last = s_last;
     __syncthreads();  // every thread has read the flag before the epilogue reuses the ring
     if (is_last == 0u) return;  // uniform over the workgroup
-    // one slot per pass, in steps of 16 or 32 floats per thread (hoisting
-    // all loads of a slot would spill the accumulators)
+    // the reduction moves 16 or 32 floats per thread per step (hoisting all
+    // loads of a slot would spill the accumulators)
     constexpr int FNG = kAccN == 16 ? (FN > 2 ? 1 : FN) : (FN > 4 ? 4 : FN);  // blocks per step
     static_assert(FN % FNG == 0, "split-K load steps");
     // Two splits on the 32 x 32 MFMA tiles (the small tiles, whose
     // accumulators leave registers to spare): only the other split's slot is
-    // read; this split's partial is still in its accumulators.  The general
-    // path below forms (0 + slot 0) + slot 1; here split 0 forms
+    // read; this split's partial is still in its accumulators.  The paths
+    // below form (0 + partial 0) + partial 1; here split 0 forms
     // (0 + acc) + slot 1 and split 1 forms (0 + slot 0) + acc, the same bits
     // (a + b == b + a exactly), so the result still does not depend on which
     // split arrived last.  The loads of each step are issued one step

@@ -204,3 +204,31 @@ def test_split_k_arrivals_over_many_rounds():
         assert np.array_equal(got, ref.out), \
             f"execution {rep}: {int((got != ref.out).sum())} elements differ"
     r.close()
+
+
+@pytest.mark.parametrize("tile,splits", [(7, 2), (7, 4), (8, 2), (8, 3), (9, 2), (9, 3)])
+def test_float_result_does_not_depend_on_arrival(tile, splits):
+    """Normal inputs, five executions of one split plan on one workspace.
+    Which split arrives last differs from tile to tile and from run to run;
+    that split takes its own partial from its registers and reads the
+    others' from their slots, but every element sums the partials in split
+    order, so each execution gives the same bits (on the one-ahead path of
+    the 256 x 128 tile, the general path of the 256 x 256 tile, and the
+    two-split and general paths of the 64 x 64 x 128 tile)."""
+    import torch
+    c = wl.random_case(520, 392, 2200, "f16", "GELU_BIAS", True, True, 3950 + 10 * tile + splits)
+    r = DeviceRun(c, splits=splits, tile=tile)
+    say("arrival", tile, splits, r.info)
+    assert f"splits={splits}" in r.info, r.info
+    first = None
+    for rep in range(5):
+        r.out.view(torch.int16).fill_(0x7E00)
+        r.run()
+        got = r.out_bits()
+        if first is None:
+            first = got
+            check_out(c, got, oracle_of(c), label=f"tile{tile} s{splits}")
+        else:
+            assert np.array_equal(got, first), \
+                f"execution {rep}: {int((got != first).sum())} elements differ"
+    r.close()
